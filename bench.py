@@ -1,0 +1,306 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X routing library (one GPU).
+
+A step is one call of the whole routing path (sigmoid, bias, grouped top-k,
+weights, pack/relabel, counts, offsets, permutation) on the long-prefill
+workload: 32768 tokens x 896 fp32 logits, Zipf-skewed bias, rank range
+[0, 112) -> 128 output ids. Inputs rotate over three seeded sets (3 x 117 MB
+of logits) so they cannot be served from the 256 MB last-level cache.
+
+Also reported: decode latency (us per call at 8, 16 and 64 tokens, eager and
+replayed from a HIP graph), the router GEMM + route at 64 and 4096 tokens,
+the roofline of the route kernel (timed live with HIP events on the launch
+stream), and the CPU oracle timed on a bounded sample of the same workload.
+
+Prints ONE JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import platform
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "routing µs/call at 8/16/64 tokens; routed tokens/s + HBM GB/s at 32K tokens"
+HBM_PEAK_GBPS = 8000.0
+BYTES_PER_TOKEN_PATH = 3904     # logits 3584 + ids, weights, packed, perm, inv (5 x 64)
+BYTES_PER_TOKEN_ROUTE_KERNEL = 3776  # logits 3584 + ids, weights, packed (3 x 64)
+PROFILE_PMC = os.path.join(ROOT, "profiles", "pmc_route_tiles_long_prefill_32768.txt")
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--decode-calls", type=int, default=1000)
+    ap.add_argument("--oracle-seconds", type=float, default=12.0)
+    ap.add_argument("--skip-oracle", action="store_true")
+    return ap.parse_args()
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "moe_expert_routing_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as fh:
+            h.update(name.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(digest: str):
+    """HBM bytes per launch of the route kernel from the committed rocprofv3
+    --pmc summary, if it was taken on the current kernel sources."""
+    if not os.path.exists(PROFILE_PMC):
+        return None
+    kv = {}
+    with open(PROFILE_PMC) as fh:
+        for line in fh:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_digest") != digest:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class HipEvents:
+    """Raw hipEvent_t handles through the HIP runtime (for the kernel hook)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        assert self.hip.hipEventCreate(ctypes.byref(ev)) == 0
+        return ev.value
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+    def destroy(self, ev):
+        self.hip.hipEventDestroy(ev)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(this library has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_expert_routing_amd as M
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    M.lib()  # fail loudly if the HIP library is missing
+    torch.cuda.set_device(dev)
+
+    # ------------------------------------------------------------------
+    # long prefill: 32768 tokens, 3 rotating input sets
+    # ------------------------------------------------------------------
+    T = 32768
+    log("bench: generating the long-prefill inputs (3 sets)")
+    cases = [W.long_prefill(T, variant=v) for v in range(3)]
+    lg = [torch.from_numpy(c.logits).to(dev) for c in cases]
+    bs = [torch.from_numpy(c.bias).to(dev) for c in cases]
+    off, cnt = cases[0].off, cases[0].cnt
+    e_out = M.local_num_experts(W.E, W.K, off, cnt)
+    out = M.alloc_outputs(T, W.K, e_out, dev)
+    ws = M.workspace(dev, M.lib().moe_route_workspace_bytes(T, e_out, W.K))
+
+    def step(i):
+        M.route_local(lg[i % 3], bs[i % 3], off, cnt, out=out, ws=ws)
+
+    log(f"bench: warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    he = HipEvents()
+    pairs = [(he.create(), he.create()) for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    log(f"bench: timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(args.steps):
+        M.set_kernel_events(*pairs[i])
+        step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    M.set_kernel_events(None, None)
+    total_ms = t0.elapsed_time(t1)
+    ms_per_step = total_ms / args.steps
+    kern_ms = [he.elapsed_ms(a, b) for a, b in pairs]
+    for a, b in pairs:
+        he.destroy(a)
+        he.destroy(b)
+    kern_avg_ms = sum(kern_ms) / len(kern_ms)
+    tokens_per_s = T / (ms_per_step * 1e-3)
+    path_gbps = BYTES_PER_TOKEN_PATH * T / (ms_per_step * 1e-3) / 1e9
+    kern_gbps = BYTES_PER_TOKEN_ROUTE_KERNEL * T / (kern_avg_ms * 1e-3) / 1e9
+    digest = source_digest()
+    traffic = read_traffic(digest)
+    log(f"bench: {ms_per_step * 1e3:.1f} us/step, route kernel {kern_avg_ms * 1e3:.1f} us")
+
+    # ------------------------------------------------------------------
+    # decode latency
+    # ------------------------------------------------------------------
+    def time_calls(fn, n, reps=5):
+        vals = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record()
+            for _ in range(n):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            vals.append(a.elapsed_time(b) * 1e3 / n)
+        return statistics.median(vals)
+
+    def time_graph(fn, n, reps=5):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for _ in range(3):
+                fn()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        per_graph = 100
+        with torch.cuda.graph(g):
+            for _ in range(per_graph):
+                fn()
+        torch.cuda.synchronize()
+        return time_calls(g.replay, max(1, n // per_graph), reps) / per_graph
+
+    decode = {}
+    decode_graph = {}
+    decode_cases = {8: W.tiny_global(8), 16: W.decode_local(16), 64: W.decode_sweep(64, 0)}
+    for Td, c in decode_cases.items():
+        log(f"bench: decode T={Td}")
+        dl = torch.from_numpy(c.logits).to(dev)
+        db = torch.from_numpy(c.bias).to(dev)
+        eo = M.local_num_experts(W.E, W.K, c.off, c.cnt) or W.E
+        dout = M.alloc_outputs(Td, W.K, eo, dev)
+        dws = torch.zeros(1 << 16, dtype=torch.uint8, device=dev)
+        fn = (lambda dl=dl, db=db, c=c, dout=dout, dws=dws:
+              M.route_local(dl, db, c.off, c.cnt, out=dout, ws=dws))
+        fn()
+        decode[f"T{Td}"] = round(time_calls(fn, args.decode_calls), 2)
+        try:
+            decode_graph[f"T{Td}"] = round(time_graph(fn, args.decode_calls), 2)
+        except Exception as exc:  # graph capture is optional for the report
+            decode_graph[f"T{Td}"] = f"unavailable: {type(exc).__name__}"
+
+    # ------------------------------------------------------------------
+    # router GEMM + route
+    # ------------------------------------------------------------------
+    gemm = {}
+    for Tg in (64, 4096):
+        log(f"bench: router GEMM + route T={Tg}")
+        c = W.router_case(Tg)
+        hid = torch.from_numpy(c.hidden.view(np.int16)).to(dev)
+        wt = torch.from_numpy(c.weight.view(np.int16)).to(dev)
+        gb = torch.from_numpy(c.bias).to(dev)
+        glog = torch.empty((Tg, W.E), dtype=torch.float32, device=dev)
+        gout = M.alloc_outputs(Tg, W.K, W.E, dev)
+        gws = M.workspace(dev, M.lib().moe_router_gemm_route_workspace_bytes(Tg, W.H, W.E, W.E,
+                                                                              W.K))
+        fn = (lambda hid=hid, wt=wt, gb=gb, glog=glog, gout=gout, gws=gws:
+              M.router_gemm_route(hid, wt, gb, logits=glog, out=gout, ws=gws))
+        fn()
+        us = time_calls(fn, 200 if Tg == 64 else 50)
+        flops = 2.0 * Tg * W.E * W.H
+        gemm[f"T{Tg}"] = {"us_per_call": round(us, 2),
+                          "tflops_incl_route": round(flops / (us * 1e-6) / 1e12, 2)}
+
+    # ------------------------------------------------------------------
+    # CPU oracle on a bounded sample of the same workload
+    # ------------------------------------------------------------------
+    cpu = None
+    if not args.skip_oracle:
+        import oracle as O
+        c0 = cases[0]
+        chunk = 1024
+        done = 0
+        log(f"bench: oracle on the host (about {args.oracle_seconds:.0f} s)")
+        t_start = time.perf_counter()
+        while done < T and time.perf_counter() - t_start < args.oracle_seconds:
+            O.route_ref(c0.logits[done:done + chunk], c0.bias,
+                        local_expert_offset=off, num_local_experts=cnt)
+            done += chunk
+        el = time.perf_counter() - t_start
+        cpu = {"value": round(done / el, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"first {done} of the {T} long-prefill tokens, routed in chunks of "
+                         f"{chunk} tokens (each chunk a full oracle call incl. permutation), "
+                         f"{el:.1f} s single-threaded Python+numpy on "
+                         f"{platform.processor() or platform.machine()}, "
+                         f"{os.cpu_count()} host cores present"}
+
+    frac = kern_gbps / HBM_PEAK_GBPS
+    res = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "long_prefill_32768x896_zipf_bias_range_0_112",
+                   "tokens": T, "num_experts": W.E, "n_groups": W.G, "topk_group": W.TG,
+                   "top_k": W.K, "local_expert_offset": off, "num_local_experts": cnt,
+                   "num_experts_out": e_out, "input_sets_rotated": 3},
+        "hbm_gbps_algorithmic_path": round(path_gbps, 1),
+        "decode_us_per_call": decode,
+        "decode_us_per_call_hipgraph": decode_graph,
+        "router_gemm_route": gemm,
+        "roofline": {"bound": "hbm", "kernel": "route_tiles_kernel",
+                     "achieved": round(kern_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(frac, 4),
+                     "kernel_us_avg": round(kern_avg_ms * 1e3, 2),
+                     "bytes_per_token": BYTES_PER_TOKEN_ROUTE_KERNEL,
+                     "traffic": (round(traffic, 0) if traffic is not None else None),
+                     "source_digest": digest},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,191 @@
+/*
+ * moe_route.h - C ABI of the MI355X (gfx950) routed-MoE routing library.
+ *
+ * The library computes, per token, the routing step of a large-expert routed
+ * MoE: a sigmoid router with a correction bias and a grouped top-k ("[ROCm]
+ * [Perf] Kimi-K3: token-sharded residual stream for long prefills", author's
+ * reply on shard-routed test coverage), the renormalised weights, the packed
+ * routed entries (expert id in bits 31..16, bf16 weight in bits 15..0) with
+ * the optional rank-local relabel of the pack epilogue, and the per-expert
+ * counts, exclusive offsets and expert-major permutation that the expert
+ * GEMMs consume ("[kimi-k3] Rank-local expert ids for the EP routed MoE
+ * (upstream #45544)", commit message, passages on the fused route+quant
+ * launch and its plumbing).
+ *
+ * Conventions shared by every entry point:
+ *  - Tensor pointers are DEVICE pointers owned by the caller; buffers are
+ *    row-major and contiguous. The library allocates nothing.
+ *  - `stream` is a hipStream_t (NULL = the null stream). Calls are
+ *    asynchronous on it: no host synchronisation, no device-to-host reads.
+ *  - Arguments are validated on the host before anything is launched. On a
+ *    negative return nothing has been written.
+ *  - Logits must be finite; NaN or infinity is outside the contract and is
+ *    not detected.
+ *  - Results are deterministic: the same inputs give the same bits on every
+ *    call, and no atomic operation decides an order.
+ */
+#ifndef MOE_ROUTE_H
+#define MOE_ROUTE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Largest token count routed by the single-launch decode path (the fused
+ * launch's token cap on the pages is 64 tokens, and that cap is public).
+ * Larger calls run the tiled prefill path; both give identical results. */
+#define MOE_ROUTE_MAX_FUSED_TOKENS 64
+
+/* Envelope of the kernels (outside it calls return MOE_ERR_UNSUPPORTED):
+ * num_experts a multiple of 128 and at most 1024; n_groups a power of two
+ * with 1 <= n_groups <= 64; 1 <= topk_group <= n_groups;
+ * 1 <= top_k <= min(32, topk_group * num_experts / n_groups);
+ * group_topn 1 or 2. */
+#define MOE_ROUTE_MAX_EXPERTS 1024
+#define MOE_ROUTE_MAX_TOPK 32
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_NULL = -1,        /* a required pointer is NULL                    */
+  MOE_ERR_SHAPE = -2,       /* negative size, or shape inconsistent          */
+  MOE_ERR_RANGE = -3,       /* expert range outside [0, num_experts)         */
+  MOE_ERR_UNSUPPORTED = -4, /* parameters outside the kernels' envelope      */
+  MOE_ERR_WORKSPACE = -5,   /* workspace missing or too small                */
+  MOE_ERR_HIP = -6          /* a HIP launch failed                           */
+} moe_status;
+
+/* Routing parameters. The workload on the pages: 896 experts, top_k 16;
+ * grouping 8 groups of 112, keep 4, group score = sum of the group's top 2
+ * biased scores. */
+typedef struct moe_route_params {
+  int32_t num_experts; /* E                                                 */
+  int32_t n_groups;    /* G: groups of E/G consecutive experts              */
+  int32_t topk_group;  /* groups kept per token                             */
+  int32_t top_k;       /* K: experts selected per token                     */
+  int32_t group_topn;  /* group score = fp32 sum of the group's top n sp    */
+} moe_route_params;
+
+/* Output buffers. E' is the output id space: num_experts for global ids,
+ * or moe_route_local_num_experts(...) when a rank range applies. */
+typedef struct moe_route_outputs {
+  int32_t *topk_ids;     /* [T, K] global expert ids, slot k = k-th best     */
+  float *topk_weights;   /* [T, K] s_k / sum_j s_j, s = unbiased sigmoid     */
+  int32_t *packed;       /* [T, K] (id' << 16) | bf16_rne(weight)            */
+  int32_t *counts;       /* [E'] entries per output id                       */
+  int32_t *offsets;      /* [E' + 1] exclusive offsets, offsets[E'] = T*K    */
+  int32_t *perm;         /* [T*K] expert-major position -> flat index t*K+k  */
+  int32_t *inv_perm;     /* [T*K] flat index -> position (may be NULL)       */
+} moe_route_outputs;
+
+/*
+ * Output id space of a rank range: round_up(num_local_experts + top_k, 4)
+ * when the range [local_expert_offset, local_expert_offset +
+ * num_local_experts) is a proper sub-range that shrinks the routing problem
+ * (0 < count, and the rounded size is below num_experts); 0 when it does not
+ * apply (global ids are kept). The rank-local relabel and the local problem
+ * size are stated in "[kimi-k3] Rank-local expert ids for the EP routed MoE
+ * (upstream #45544)", commit message (128 at EP8 for 896 experts, top_k 16).
+ * Returns MOE_ERR_RANGE for a range outside [0, num_experts) and
+ * MOE_ERR_SHAPE for num_experts <= 0 or top_k <= 0.
+ */
+int32_t moe_route_local_num_experts(int32_t num_experts, int32_t top_k,
+                                    int32_t local_expert_offset,
+                                    int32_t num_local_experts);
+
+/*
+ * Workspace bytes needed by moe_route / moe_route_local for `num_tokens`
+ * tokens and `num_experts_out` output ids (E'). The first 256 bytes are a
+ * control block that must be zero before the workspace is first used; every
+ * call leaves it zero again. One workspace must not be used by two calls
+ * that can run at the same time.
+ */
+size_t moe_route_workspace_bytes(int32_t num_tokens, int32_t num_experts_out,
+                                 int32_t top_k);
+
+/*
+ * Route T tokens with global ids (E' = num_experts).
+ *   logits   [T, E] fp32 router logits
+ *   bias     [E]    fp32 correction bias (added for selection only)
+ * Writes every buffer of `out`. T = 0 writes zero counts and offsets.
+ * Returns MOE_OK or a negative moe_status.
+ */
+int moe_route(const float *logits, const float *bias, int32_t num_tokens,
+              const moe_route_params *params, const moe_route_outputs *out,
+              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Route T tokens for one expert-parallel rank range. Identical to moe_route
+ * except for the packed ids and the permutation space: when the range
+ * applies (moe_route_local_num_experts > 0), experts of the range are
+ * written as id - local_expert_offset, and any other expert chosen in top-k
+ * slot k as num_local_experts + k (unique within a row); counts, offsets and
+ * perm cover the E' = round_up(count + top_k, 4) output ids. topk_ids stay
+ * global. num_local_experts = 0 keeps global ids.
+ */
+int moe_route_local(const float *logits, const float *bias,
+                    int32_t num_tokens, const moe_route_params *params,
+                    int32_t local_expert_offset, int32_t num_local_experts,
+                    const moe_route_outputs *out, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
+/*
+ * Workspace bytes needed by moe_router_gemm_route (router GEMM staging plus
+ * the routing workspace).
+ */
+size_t moe_router_gemm_route_workspace_bytes(int32_t num_tokens, int32_t hidden,
+                                             int32_t num_experts,
+                                             int32_t num_experts_out,
+                                             int32_t top_k);
+
+/*
+ * Router GEMM followed by routing: logits = hidden . W^T with bf16 operands
+ * and fp32 accumulation on the matrix cores, then moe_route_local on them.
+ * The router is a [num_experts, hidden] matrix replicated on every rank
+ * ("feat(kimi): tensor- and expert-parallel sharding for the K3.1 decoder",
+ * memory table: router 0.59 B parameters).
+ *   hidden_bf16 [T, H] bf16 bit patterns, weight_bf16 [E, H] bf16 bit
+ *   patterns, H a multiple of 64; logits_out [T, E] fp32 (required: the
+ *   routing reads the logits from it).
+ */
+int moe_router_gemm_route(const uint16_t *hidden_bf16,
+                          const uint16_t *weight_bf16, int32_t num_tokens,
+                          int32_t hidden, const float *bias, float *logits_out,
+                          const moe_route_params *params,
+                          int32_t local_expert_offset,
+                          int32_t num_local_experts,
+                          const moe_route_outputs *out, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/*
+ * Diagnostic: y[i] = the binary32 nearest to 1 / (1 + e^-x[i]) for n
+ * elements, with the routing kernels' own sigmoid. mode 0 = the production
+ * evaluation; mode 1 = the double-double re-evaluation only (the path taken
+ * near binary32 rounding boundaries), so that tests can reach it.
+ */
+int moe_sigmoid_rn32(const float *x, float *y, int64_t n, int32_t mode,
+                     void *stream);
+
+/*
+ * Benchmark hook. When `before` and `after` are hipEvent_t handles, every
+ * later routing call records `before` on its stream just before its first
+ * routing kernel (the per-token route kernel: the single kernel of the
+ * decode path, the tile kernel of the prefill path) and `after` just after
+ * it. NULL, NULL turns recording off. Process-wide and not thread-safe; it
+ * exists so that a benchmark can time that kernel on its own stream.
+ */
+int moe_route_set_kernel_events(void *before, void *after);
+
+/* Human-readable name of a moe_status value. */
+const char *moe_route_status_string(int status);
+
+/* ABI version of this header (major * 100 + minor). */
+int32_t moe_route_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_ROUTE_H */

@@ -1,0 +1,258 @@
+"""Python binding of libmoe_route.so: the MI355X routed-MoE routing step.
+
+Argument marshalling only. Every step of the routing runs in the HIP
+kernels behind the C ABI of ``include/moe_route.h``; this module passes
+``tensor.data_ptr()`` values and the current HIP stream, allocates output
+tensors and a cached workspace when the caller gives none, and turns a
+negative status into an exception. There is no CPU fallback: without the
+built library every call raises.
+
+Calls (same names as the C ABI):
+    route(logits, bias, ...)                       -> moe_route
+    route_local(logits, bias, off, cnt, ...)       -> moe_route_local
+    router_gemm_route(hidden, weight, bias, ...)   -> moe_router_gemm_route
+    local_num_experts(E, K, off, cnt)              -> moe_route_local_num_experts
+    sigmoid_rn32(x, mode=0)                        -> moe_sigmoid_rn32 (diagnostic)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "_lib", "libmoe_route.so")
+
+MAX_FUSED_TOKENS = 64
+
+_c_i32 = ctypes.c_int32
+_c_vp = ctypes.c_void_p
+
+
+class RouteParams(ctypes.Structure):
+    _fields_ = [("num_experts", _c_i32), ("n_groups", _c_i32), ("topk_group", _c_i32),
+                ("top_k", _c_i32), ("group_topn", _c_i32)]
+
+
+class RouteOutputs(ctypes.Structure):
+    _fields_ = [("topk_ids", _c_vp), ("topk_weights", _c_vp), ("packed", _c_vp),
+                ("counts", _c_vp), ("offsets", _c_vp), ("perm", _c_vp), ("inv_perm", _c_vp)]
+
+
+EXPORTS = {
+    "moe_route_abi_version": (_c_i32, []),
+    "moe_route_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "moe_route_local_num_experts": (_c_i32, [_c_i32, _c_i32, _c_i32, _c_i32]),
+    "moe_route_workspace_bytes": (ctypes.c_size_t, [_c_i32, _c_i32, _c_i32]),
+    "moe_route": (ctypes.c_int, [_c_vp, _c_vp, _c_i32, ctypes.POINTER(RouteParams),
+                                 ctypes.POINTER(RouteOutputs), _c_vp, ctypes.c_size_t, _c_vp]),
+    "moe_route_local": (ctypes.c_int, [_c_vp, _c_vp, _c_i32, ctypes.POINTER(RouteParams),
+                                       _c_i32, _c_i32, ctypes.POINTER(RouteOutputs), _c_vp,
+                                       ctypes.c_size_t, _c_vp]),
+    "moe_router_gemm_route_workspace_bytes": (ctypes.c_size_t,
+                                              [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
+    "moe_router_gemm_route": (ctypes.c_int, [_c_vp, _c_vp, _c_i32, _c_i32, _c_vp, _c_vp,
+                                             ctypes.POINTER(RouteParams), _c_i32, _c_i32,
+                                             ctypes.POINTER(RouteOutputs), _c_vp,
+                                             ctypes.c_size_t, _c_vp]),
+    "moe_sigmoid_rn32": (ctypes.c_int, [_c_vp, _c_vp, ctypes.c_int64, _c_i32, _c_vp]),
+    "moe_route_set_kernel_events": (ctypes.c_int, [_c_vp, _c_vp]),
+}
+
+_LIB = None
+
+
+class MoeRouteError(RuntimeError):
+    pass
+
+
+def lib() -> ctypes.CDLL:
+    """Load the built HIP library (raises if it was not built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise MoeRouteError(
+                f"{LIB_PATH} is missing: build it with `python -m moe_expert_routing_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in EXPORTS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = handle
+    return _LIB
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        msg = lib().moe_route_status_string(status).decode()
+        raise MoeRouteError(f"{what} failed: {msg} ({status})")
+
+
+def local_num_experts(num_experts: int, top_k: int, local_expert_offset: int,
+                      num_local_experts: int) -> int:
+    v = lib().moe_route_local_num_experts(num_experts, top_k, local_expert_offset,
+                                          num_local_experts)
+    if v < 0:
+        _check(v, "moe_route_local_num_experts")
+    return int(v)
+
+
+def _stream_handle(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+_WORKSPACES: Dict[int, torch.Tensor] = {}
+
+
+def workspace(device: torch.device, nbytes: int) -> torch.Tensor:
+    """A zero-initialised byte buffer of at least nbytes, cached per device.
+    Its control block is zero when allocated and every call leaves it zero."""
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    ws = _WORKSPACES.get(idx)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1 << 16), dtype=torch.uint8, device=device)
+        _WORKSPACES[idx] = ws
+    return ws
+
+
+def alloc_outputs(T: int, top_k: int, e_out: int, device: torch.device,
+                  with_inv: bool = True) -> Dict[str, torch.Tensor]:
+    i32 = dict(dtype=torch.int32, device=device)
+    out = {
+        "topk_ids": torch.empty((T, top_k), **i32),
+        "topk_weights": torch.empty((T, top_k), dtype=torch.float32, device=device),
+        "packed": torch.empty((T, top_k), **i32),
+        "counts": torch.empty((e_out,), **i32),
+        "offsets": torch.empty((e_out + 1,), **i32),
+        "perm": torch.empty((T * top_k,), **i32),
+        "inv_perm": torch.empty((T * top_k,), **i32) if with_inv else None,
+    }
+    return out
+
+
+def _outputs_struct(out: Dict[str, torch.Tensor]) -> RouteOutputs:
+    def p(name):
+        t = out.get(name)
+        return t.data_ptr() if t is not None and t.numel() > 0 else None
+    return RouteOutputs(p("topk_ids"), p("topk_weights"), p("packed"), p("counts"),
+                        p("offsets"), p("perm"), p("inv_perm"))
+
+
+def _require(t: torch.Tensor, name: str, dtype, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise MoeRouteError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype or t.dim() != ndim or not t.is_contiguous():
+        raise MoeRouteError(f"{name} must be a contiguous {ndim}-d {dtype} tensor")
+
+
+def _params(E, n_groups, topk_group, top_k, group_topn) -> RouteParams:
+    return RouteParams(E, n_groups, topk_group, top_k, group_topn)
+
+
+def route_local(logits: torch.Tensor, bias: torch.Tensor, local_expert_offset: int = 0,
+                num_local_experts: int = 0, *, n_groups: int = 8, topk_group: int = 4,
+                top_k: int = 16, group_topn: int = 2,
+                out: Optional[Dict[str, torch.Tensor]] = None,
+                ws: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """moe_route_local over torch tensors; returns the output tensors."""
+    _require(logits, "logits", torch.float32, 2)
+    _require(bias, "bias", torch.float32, 1)
+    T, E = logits.shape
+    if bias.shape[0] != E:
+        raise MoeRouteError("bias must have num_experts elements")
+    e_loc = local_num_experts(E, top_k, local_expert_offset, num_local_experts)
+    e_out = e_loc if e_loc > 0 else E
+    dev = logits.device
+    if out is None:
+        out = alloc_outputs(T, top_k, e_out, dev)
+    need = lib().moe_route_workspace_bytes(T, e_out, top_k)
+    if ws is None:
+        ws = workspace(dev, need)
+    prm = _params(E, n_groups, topk_group, top_k, group_topn)
+    o = _outputs_struct(out)
+    st = lib().moe_route_local(logits.data_ptr(), bias.data_ptr(), T, ctypes.byref(prm),
+                               local_expert_offset, num_local_experts, ctypes.byref(o),
+                               ws.data_ptr(), ws.numel(), _stream_handle(dev))
+    _check(st, "moe_route_local")
+    out["num_experts_out"] = e_out
+    return out
+
+
+def route(logits: torch.Tensor, bias: torch.Tensor, *, n_groups: int = 8, topk_group: int = 4,
+          top_k: int = 16, group_topn: int = 2, out: Optional[Dict[str, torch.Tensor]] = None,
+          ws: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """moe_route (global ids) over torch tensors."""
+    _require(logits, "logits", torch.float32, 2)
+    _require(bias, "bias", torch.float32, 1)
+    T, E = logits.shape
+    dev = logits.device
+    if out is None:
+        out = alloc_outputs(T, top_k, E, dev)
+    need = lib().moe_route_workspace_bytes(T, E, top_k)
+    if ws is None:
+        ws = workspace(dev, need)
+    prm = _params(E, n_groups, topk_group, top_k, group_topn)
+    o = _outputs_struct(out)
+    st = lib().moe_route(logits.data_ptr(), bias.data_ptr(), T, ctypes.byref(prm),
+                         ctypes.byref(o), ws.data_ptr(), ws.numel(), _stream_handle(dev))
+    _check(st, "moe_route")
+    out["num_experts_out"] = E
+    return out
+
+
+def router_gemm_route(hidden: torch.Tensor, weight: torch.Tensor, bias: torch.Tensor,
+                      local_expert_offset: int = 0, num_local_experts: int = 0, *,
+                      n_groups: int = 8, topk_group: int = 4, top_k: int = 16,
+                      group_topn: int = 2, logits: Optional[torch.Tensor] = None,
+                      out: Optional[Dict[str, torch.Tensor]] = None,
+                      ws: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """moe_router_gemm_route: bf16 hidden [T, H] . bf16 weight [E, H]^T -> fp32
+    logits, then routing. hidden/weight may be bfloat16 or int16/uint16 bit
+    patterns."""
+    for t, n in ((hidden, "hidden"), (weight, "weight")):
+        if not t.is_cuda or t.dim() != 2 or not t.is_contiguous() or t.element_size() != 2:
+            raise MoeRouteError(f"{n} must be a contiguous 2-d 16-bit GPU tensor")
+    _require(bias, "bias", torch.float32, 1)
+    T, H = hidden.shape
+    E = weight.shape[0]
+    if weight.shape[1] != H or bias.shape[0] != E:
+        raise MoeRouteError("inconsistent router GEMM shapes")
+    dev = hidden.device
+    e_loc = local_num_experts(E, top_k, local_expert_offset, num_local_experts)
+    e_out = e_loc if e_loc > 0 else E
+    if logits is None:
+        logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    _require(logits, "logits", torch.float32, 2)
+    if out is None:
+        out = alloc_outputs(T, top_k, e_out, dev)
+    need = lib().moe_router_gemm_route_workspace_bytes(T, H, E, e_out, top_k)
+    if ws is None:
+        ws = workspace(dev, need)
+    prm = _params(E, n_groups, topk_group, top_k, group_topn)
+    o = _outputs_struct(out)
+    st = lib().moe_router_gemm_route(hidden.data_ptr(), weight.data_ptr(), T, H,
+                                      bias.data_ptr(), logits.data_ptr(), ctypes.byref(prm),
+                                      local_expert_offset, num_local_experts, ctypes.byref(o),
+                                      ws.data_ptr(), ws.numel(), _stream_handle(dev))
+    _check(st, "moe_router_gemm_route")
+    out["logits"] = logits
+    out["num_experts_out"] = e_out
+    return out
+
+
+def set_kernel_events(before: Optional[int], after: Optional[int]) -> None:
+    """Benchmark hook: record two hipEvent_t handles around the route kernel
+    of every later call (None, None turns it off)."""
+    _check(lib().moe_route_set_kernel_events(before, after), "moe_route_set_kernel_events")
+
+
+def sigmoid_rn32(x: torch.Tensor, mode: int = 0) -> torch.Tensor:
+    """Diagnostic: the kernels' correctly rounded sigmoid over a 1-d tensor."""
+    _require(x, "x", torch.float32, 1)
+    y = torch.empty_like(x)
+    st = lib().moe_sigmoid_rn32(x.data_ptr(), y.data_ptr(), x.numel(), mode,
+                                _stream_handle(x.device))
+    _check(st, "moe_sigmoid_rn32")
+    return y

@@ -1,0 +1,221 @@
+"""GPU parity of the HIP routing path against the CPU oracle, through the C
+ABI, on every workload and on edge cases."""
+import numpy as np
+import pytest
+import torch
+
+import moe_expert_routing_amd as M
+import oracle as O
+import workloads as W
+from gpu_util import DEV, assert_parity, oracle_case, run_case, say, to_dev
+
+pytestmark = [
+    pytest.mark.gpu,
+    pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU"),
+]
+
+
+# --------------------------------------------------------------------------
+# sigmoid (diagnostic entry point): bit-exact against the oracle
+# --------------------------------------------------------------------------
+
+def _hard_sigmoid_inputs(n_keep=4000):
+    """Inputs whose binary64 sigmoid lies closest to a binary32 rounding
+    boundary (found by a strided sweep), plus saturation and subnormal
+    regions."""
+    u = np.arange(0, 1 << 23, dtype=np.uint32) * np.uint32(509) + np.uint32(0x3C000000)
+    x = u.view(np.float32)
+    x = np.concatenate([x, -x])
+    x = x[np.isfinite(x) & (np.abs(x) < 60)]
+    d = 1.0 / (1.0 + np.exp(-x.astype(np.float64)))
+    f = d.astype(np.float32)
+    ulp = np.nextafter(f, np.float32(np.inf)).astype(np.float64) - f.astype(np.float64)
+    frac = np.abs(np.abs(d - f.astype(np.float64)) / ulp - 0.5)
+    hard = x[np.argsort(frac)[:n_keep]]
+    extra = np.concatenate([
+        np.linspace(-115, -80, 3001, dtype=np.float32),
+        np.linspace(15, 45, 1001, dtype=np.float32),
+        np.array([0.0, -0.0, 1e-30, -1e-30, 3e38, -3e38, 40.0, -110.0], np.float32),
+    ])
+    return np.concatenate([hard, extra]).astype(np.float32)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_sigmoid_bit_exact(mode):
+    rng = np.random.default_rng(77)
+    x = np.concatenate([rng.standard_normal(200000).astype(np.float32),
+                        (8 * rng.standard_normal(50000)).astype(np.float32),
+                        _hard_sigmoid_inputs()])
+    say(f"sigmoid mode={mode} n={x.size}")
+    y = M.sigmoid_rn32(to_dev(x), mode=mode).cpu().numpy()
+    want = O.sigmoid_rn32(x)
+    bad = np.nonzero(y.view(np.uint32) != want.view(np.uint32))[0]
+    assert bad.size == 0, [(float(x[i]), float(y[i]), float(want[i])) for i in bad[:5]]
+
+
+# --------------------------------------------------------------------------
+# workloads
+# --------------------------------------------------------------------------
+
+def test_tiny_global_8_tokens():
+    c = W.tiny_global()
+    say("case tiny_global T=8")
+    assert_parity(run_case(c), oracle_case(c), c.name)
+
+
+def test_decode_local_16_tokens_rank3():
+    c = W.decode_local()
+    say("case decode_local T=16 off=336 cnt=112")
+    got, want = run_case(c), oracle_case(c)
+    assert int(want["num_experts_out"]) == 128
+    assert_parity(got, want, c.name)
+
+
+@pytest.mark.parametrize("T", W.DECODE_SWEEP_T)
+def test_decode_sweep_all_ranks_with_ties(T):
+    for rank in range(W.EP):
+        c = W.decode_sweep(T, rank)
+        say(f"case {c.name}")
+        assert_parity(run_case(c), oracle_case(c), c.name)
+
+
+def test_long_prefill_32k_full():
+    c = W.long_prefill()
+    say("case long_prefill T=32768 off=0 cnt=112 (full oracle comparison)")
+    got = run_case(c)
+    want = oracle_case(c)
+    assert_parity(got, want, c.name)
+    load = np.bincount(want["topk_ids"].ravel(), minlength=896)
+    assert load.max() / load.mean() > 7.0
+
+
+@pytest.mark.parametrize("T", [64, 4096])
+def test_router_gemm_then_route(T):
+    c = W.router_case(T)
+    say(f"case router_gemm T={T}")
+    hid = to_dev(c.hidden.view(np.int16))
+    wt = to_dev(c.weight.view(np.int16))
+    out = M.router_gemm_route(hid, wt, to_dev(c.bias))
+    torch.cuda.synchronize()
+    logits = out["logits"].cpu().numpy()
+    ref = O.router_logits_ref(c.hidden, c.weight)
+    bound = O.router_logits_bound(c.hidden, c.weight)
+    err = np.abs(logits.astype(np.float64) - ref)
+    assert np.all(err <= bound), f"max err {err.max():.3g} vs bound {bound.min():.3g}"
+    got = {k: (v.cpu().numpy() if isinstance(v, torch.Tensor) else v) for k, v in out.items()}
+    want = O.route_ref(logits, c.bias)  # routing parity on the GPU's own logits
+    assert_parity(got, want, c.name)
+
+
+# --------------------------------------------------------------------------
+# edge cases
+# --------------------------------------------------------------------------
+
+def test_zero_tokens():
+    c = W.random_case(0, seed=1, off=336, cnt=112)
+    say("case T=0")
+    got = run_case(c)
+    assert got["counts"].tolist() == [0] * 128
+    assert got["offsets"].tolist() == [0] * 129
+    assert got["perm"].size == 0
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 63, 64, 65, 127, 129, 1000, 4099])
+def test_ragged_token_counts_cross_both_paths(T):
+    for off, cnt in ((0, 0), (448, 112)):
+        c = W.random_case(T, seed=500 + T, off=off, cnt=cnt)
+        say(f"case ragged T={T} off={off} cnt={cnt}")
+        assert_parity(run_case(c), oracle_case(c), c.name)
+
+
+@pytest.mark.parametrize("ep", [2, 4, 16])
+@pytest.mark.parametrize("which", ["first", "middle", "last"])
+def test_rank_ranges(ep, which):
+    cnt = 896 // ep
+    rank = {"first": 0, "middle": ep // 2, "last": ep - 1}[which]
+    for T in (1, 24, 64, 200):
+        c = W.random_case(T, seed=7000 + 100 * ep + 10 * rank + T, off=rank * cnt, cnt=cnt)
+        say(f"case ep={ep} rank={rank} T={T}")
+        assert_parity(run_case(c), oracle_case(c), c.name)
+
+
+def test_range_that_does_not_apply_keeps_global_ids():
+    c = W.random_case(40, seed=91, off=0, cnt=884)  # round_up(900, 4) >= 896
+    say("case range not applying")
+    got = run_case(c)
+    assert int(got["num_experts_out"]) == 896
+    assert_parity(got, oracle_case(c), c.name)
+
+
+@pytest.mark.parametrize("E,G,TG,K,N", [
+    (896, 1, 1, 16, 2),     # plain top-k
+    (896, 8, 8, 16, 2),     # every group kept
+    (896, 8, 4, 16, 1),     # group score = group max
+    (896, 8, 2, 8, 2),
+    (256, 8, 4, 8, 2),
+    (1024, 16, 4, 32, 2),
+    (128, 64, 8, 4, 2),
+    (512, 4, 1, 32, 1),
+])
+def test_other_parameters(E, G, TG, K, N):
+    for T in (5, 130):
+        c = W.random_case(T, seed=E + G + TG + K + N + T, e=E, n_groups=G, topk_group=TG,
+                          top_k=K, group_topn=N)
+        say(f"case E={E} G={G} TG={TG} K={K} N={N} T={T}")
+        assert_parity(run_case(c), oracle_case(c), c.name)
+
+
+def test_extreme_logits_and_dense_ties():
+    rng = np.random.default_rng(3)
+    T = 96
+    logits = rng.choice(np.array([-120, -100, -95, -90, -88, -30, -1, 0, 1, 2, 30, 50],
+                                 np.float32), size=(T, 896)).astype(np.float32)
+    logits[:8] = 0.0  # every score ties: lower ids win
+    c = W.RouteCase("extreme", logits, np.zeros(896, np.float32), off=112, cnt=112)
+    say("case extreme logits")
+    assert_parity(run_case(c), oracle_case(c), c.name)
+    c2 = W.RouteCase("extreme_bias", logits, (0.01 * rng.standard_normal(896)).astype(np.float32))
+    assert_parity(run_case(c2), oracle_case(c2), c2.name)
+
+
+def test_deterministic_across_calls():
+    c = W.long_prefill(T=8192)
+    say("case determinism T=8192")
+    a = run_case(c)
+    b = run_case(c)
+    for k in ("topk_ids", "topk_weights", "packed", "counts", "offsets", "perm", "inv_perm"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_decode_and_prefill_paths_agree():
+    c = W.long_prefill(T=256)
+    say("case decode-vs-prefill")
+    big = run_case(c)
+    small_case = W.RouteCase("first64", c.logits[:64], c.bias, off=c.off, cnt=c.cnt)
+    small = run_case(small_case)
+    for k in ("topk_ids", "topk_weights", "packed"):
+        assert np.array_equal(big[k][:64], small[k]), k
+
+
+def test_global_and_local_entries_reach_the_gemm_in_the_same_order():
+    """The pages' invariant: the same (token, local expert, weight) entries in
+    the same order under global and rank-local ids."""
+    c = W.long_prefill(T=3000)
+    off, cnt = 336, 112
+    say("case global-vs-local order")
+    g = run_case(W.RouteCase("g", c.logits, c.bias))
+    loc = run_case(W.RouteCase("l", c.logits, c.bias, off=off, cnt=cnt))
+    K = 16
+
+    def entries(res, lo, hi, shift):
+        ids = res["packed"] >> 16
+        sel = []
+        for f in res["perm"]:
+            t, k = divmod(int(f), K)
+            e = int(ids[t, k])
+            if lo <= e < hi:
+                sel.append((t, e + shift, int(res["packed"][t, k] & 0xFFFF)))
+        return sel
+    assert entries(loc, 0, cnt, off) == entries(g, off, off + cnt, 0)
+    assert np.array_equal(g["topk_ids"], loc["topk_ids"])
+    assert np.array_equal(g["packed"] & 0xFFFF, loc["packed"] & 0xFFFF)
