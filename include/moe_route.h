@@ -163,7 +163,9 @@ int moe_router_gemm_route(const uint16_t *hidden_bf16,
  * Diagnostic: y[i] = the binary32 nearest to 1 / (1 + e^-x[i]) for n
  * elements, with the routing kernels' own sigmoid. mode 0 = the production
  * evaluation; mode 1 = the double-double re-evaluation only (the path taken
- * near binary32 rounding boundaries), so that tests can reach it.
+ * near binary32 rounding boundaries), so that tests can reach it; mode 2 =
+ * the fast hardware approximation the kernels use to pick candidates (NOT
+ * correctly rounded: its error bound is what tests check).
  */
 int moe_sigmoid_rn32(const float *x, float *y, int64_t n, int32_t mode,
                      void *stream);
@@ -177,6 +179,14 @@ int moe_sigmoid_rn32(const float *x, float *y, int64_t n, int32_t mode,
  * exists so that a benchmark can time that kernel on its own stream.
  */
 int moe_route_set_kernel_events(void *before, void *after);
+
+/*
+ * Diagnostic: number of tokens routed through the exact path (the fast path
+ * could not prove its answer) since the last reset, summed over calls on the
+ * current device. Synchronises with the device. reset != 0 zeroes the count.
+ * Returns the count or MOE_ERR_HIP.
+ */
+int64_t moe_route_exact_path_tokens(int32_t reset);
 
 /* Human-readable name of a moe_status value. */
 const char *moe_route_status_string(int status);

@@ -59,6 +59,7 @@ EXPORTS = {
                                              ctypes.c_size_t, _c_vp]),
     "moe_sigmoid_rn32": (ctypes.c_int, [_c_vp, _c_vp, ctypes.c_int64, _c_i32, _c_vp]),
     "moe_route_set_kernel_events": (ctypes.c_int, [_c_vp, _c_vp]),
+    "moe_route_exact_path_tokens": (ctypes.c_int64, [_c_i32]),
 }
 
 _LIB = None
@@ -246,6 +247,14 @@ def set_kernel_events(before: Optional[int], after: Optional[int]) -> None:
     """Benchmark hook: record two hipEvent_t handles around the route kernel
     of every later call (None, None turns it off)."""
     _check(lib().moe_route_set_kernel_events(before, after), "moe_route_set_kernel_events")
+
+
+def exact_path_tokens(reset: bool = False) -> int:
+    """Diagnostic: tokens routed through the exact path since the last reset."""
+    v = lib().moe_route_exact_path_tokens(1 if reset else 0)
+    if v < 0:
+        _check(int(v), "moe_route_exact_path_tokens")
+    return int(v)
 
 
 def sigmoid_rn32(x: torch.Tensor, mode: int = 0) -> torch.Tensor:

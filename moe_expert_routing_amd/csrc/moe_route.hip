@@ -26,13 +26,18 @@
 #include "internal.hpp"
 #include "route_wave.hpp"
 
+static_assert(moe::kMaxTopK == MOE_ROUTE_MAX_TOPK, "top-k capacity");
+
 namespace moe {
 
 constexpr int WAVES_PER_BLOCK = 4;
 constexpr int BLOCK = 64 * WAVES_PER_BLOCK;
-constexpr int TILE_TOKENS = 64;
-constexpr int TOKENS_PER_WAVE_PER_TILE = TILE_TOKENS / WAVES_PER_BLOCK;
 constexpr size_t CONTROL_BYTES = 256;
+// Prefill tiles: one block of 16 waves routes 16 tokens, one per wave (no
+// token loop: the per-token code keeps its registers low enough for eight
+// waves per SIMD).
+constexpr int TILE_TOKENS = 16;
+constexpr int TILE_BLOCK = 64 * TILE_TOKENS;
 
 // Exclusive scan of in[0..n) (n <= 1024, any memory) into out[0..n] in LDS,
 // out[n] = total. All BLOCK threads must call it.
@@ -80,14 +85,17 @@ __global__ __launch_bounds__(BLOCK) void route_decode_kernel(
   __shared__ unsigned long long mask[MOE_ROUTE_MAX_EXPERTS];
   __shared__ int32_t offs[MOE_ROUTE_MAX_EXPERTS + 1];
   __shared__ int32_t wave_tot[WAVES_PER_BLOCK];
+  __shared__ WaveScratch scratch[WAVES_PER_BLOCK];
   __shared__ int is_last;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int t = blockIdx.x * WAVES_PER_BLOCK + wave;
   if (t < T) {
-    float b[2 * NP];
+    const float *row = logits + (size_t)t * p.E;
+    float b[2 * NP], x[2 * NP];
+    load_lane_layout<NP>(row, p, lane, x);
     load_lane_layout<NP>(bias, p, lane, b);
-    route_token_wave<NP>(logits + (size_t)t * p.E, b, p, lane, t, ids, wts, packed);
+    route_token<NP>(row, x, b, bias, p, lane, t, &scratch[wave], ids, wts, packed);
   }
   // Publish this block's outputs, then take a ticket.
   __threadfence();
@@ -127,78 +135,94 @@ __global__ __launch_bounds__(BLOCK) void route_decode_kernel(
 // Prefill path, kernel 1: route tiles of 64 tokens.
 // ---------------------------------------------------------------------------
 template <int NP>
-__global__ __launch_bounds__(BLOCK) void route_tiles_kernel(
+__global__ __launch_bounds__(TILE_BLOCK) void route_tiles_kernel(
     const float *__restrict__ logits, const float *__restrict__ bias, int T, RouteParams p,
-    int ntiles, int32_t *__restrict__ ids, float *__restrict__ wts,
-    int32_t *__restrict__ packed, int32_t *__restrict__ hist, int32_t *__restrict__ tile_rank) {
-  __shared__ unsigned long long mask[MOE_ROUTE_MAX_EXPERTS];
+    int32_t *__restrict__ ids, float *__restrict__ wts, int32_t *__restrict__ packed,
+    int32_t *__restrict__ hist, int ntiles, int32_t *__restrict__ tile_rank) {
+  __shared__ uint32_t mask[MOE_ROUTE_MAX_EXPERTS];  // bit w: token w of the tile
   __shared__ int16_t idp_sh[TILE_TOKENS][MOE_ROUTE_MAX_TOPK];
+  __shared__ WaveScratch scratch[TILE_TOKENS];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  float b[2 * NP];
-  load_lane_layout<NP>(bias, p, lane, b);
-  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    for (int i = threadIdx.x; i < p.e_out; i += BLOCK) mask[i] = 0ull;
-    __syncthreads();
-#pragma unroll 1
-    for (int j = 0; j < TOKENS_PER_WAVE_PER_TILE; ++j) {
-      const int tl = wave * TOKENS_PER_WAVE_PER_TILE + j;
-      const int t = tile * TILE_TOKENS + tl;
-      if (t < T) {
-        const int idp = route_token_wave<NP>(logits + (size_t)t * p.E, b, p, lane, t, ids, wts,
-                                             packed);
-        if (lane < p.K) {
-          atomicOr(&mask[idp], 1ull << tl);
-          idp_sh[tl][lane] = (int16_t)idp;
-        }
-      }
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int tile = blockIdx.x;
+  const int t = tile * TILE_TOKENS + wave;
+  for (int i = threadIdx.x; i < p.e_out; i += TILE_BLOCK) mask[i] = 0u;
+  __syncthreads();
+  if (t < T) {
+    const float *row = logits + (size_t)t * p.E;
+    float b[2 * NP], x[2 * NP];
+    load_lane_layout<NP>(row, p, lane, x);
+    load_lane_layout<NP>(bias, p, lane, b);
+    const int idp = route_token<NP>(row, x, b, bias, p, lane, t, &scratch[wave], ids, wts, packed);
+    if (lane < p.K) {
+      atomicOr(&mask[idp], 1u << wave);
+      idp_sh[wave][lane] = (int16_t)idp;
     }
-    __syncthreads();
-    for (int i = threadIdx.x; i < p.e_out; i += BLOCK)
-      hist[(size_t)i * ntiles + tile] = __popcll(mask[i]);
-    // rank of each entry among the tile's entries with the same output id
-    const int nt = min(TILE_TOKENS, T - tile * TILE_TOKENS);
-    for (int q = threadIdx.x; q < nt * p.K; q += BLOCK) {
-      const int tl = q / p.K, k = q - tl * p.K;
-      const int idp = idp_sh[tl][k];
-      tile_rank[((size_t)tile * TILE_TOKENS + tl) * p.K + k] =
-          __popcll(mask[idp] & ((1ull << tl) - 1ull));
-    }
-    __syncthreads();
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < p.e_out; i += TILE_BLOCK)
+    hist[(size_t)i * ntiles + tile] = __popc(mask[i]);
+  // rank of each entry among the tile's entries with the same output id
+  const int nt = min(TILE_TOKENS, T - tile * TILE_TOKENS);
+  for (int q = threadIdx.x; q < nt * p.K; q += TILE_BLOCK) {
+    const int tl = q / p.K, k = q - tl * p.K;
+    tile_rank[((size_t)tile * TILE_TOKENS + tl) * p.K + k] =
+        __popc(mask[idp_sh[tl][k]] & ((1u << tl) - 1u));
   }
 }
 
-// Prefill path, kernel 2: per output id, exclusive scan over tiles.
-__global__ __launch_bounds__(64) void tile_prefix_kernel(int32_t *__restrict__ hist, int ntiles,
-                                                         int32_t *__restrict__ counts) {
+// Prefill path, kernel 2: per output id, exclusive scan over tiles (in
+// place) and the id's total -> counts. One block per id; each thread scans a
+// contiguous run of PREFIX_RUN tiles, so a wave reads 2 KB contiguously.
+constexpr int PREFIX_RUN = 8;
+__global__ __launch_bounds__(BLOCK) void tile_prefix_kernel(int32_t *__restrict__ hist, int ntiles,
+                                                            int32_t *__restrict__ counts) {
+  __shared__ int32_t wave_tot[WAVES_PER_BLOCK];
   int32_t *row = hist + (size_t)blockIdx.x * ntiles;
-  const int lane = threadIdx.x;
-  const int chunk = (ntiles + 63) / 64;
-  const int beg = min(lane * chunk, ntiles);
-  const int end = min(beg + chunk, ntiles);
-  int s = 0;
-  for (int i = beg; i < end; ++i) s += row[i];
-  int incl = s;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int carry = 0;
+  for (int base = 0; base < ntiles; base += BLOCK * PREFIX_RUN) {
+    const int beg = base + tid * PREFIX_RUN;
+    int v[PREFIX_RUN];
+    int s = 0;
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(incl, d);
-    if (lane >= d) incl += o;
+    for (int k = 0; k < PREFIX_RUN; ++k) {
+      v[k] = (beg + k < ntiles) ? row[beg + k] : 0;
+      s += v[k];
+    }
+    int incl = s;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl, d);
+      if (lane >= d) incl += o;
+    }
+    if (lane == 63) wave_tot[wv] = incl;
+    __syncthreads();
+    int off = carry;
+    int total = 0;
+#pragma unroll
+    for (int w = 0; w < WAVES_PER_BLOCK; ++w) {
+      if (w < wv) off += wave_tot[w];
+      total += wave_tot[w];
+    }
+    int run = off + incl - s;
+#pragma unroll
+    for (int k = 0; k < PREFIX_RUN; ++k) {
+      if (beg + k < ntiles) row[beg + k] = run;
+      run += v[k];
+    }
+    carry += total;
+    __syncthreads();
   }
-  int run = incl - s;
-  for (int i = beg; i < end; ++i) {
-    const int v = row[i];
-    row[i] = run;
-    run += v;
-  }
-  if (lane == 63) counts[blockIdx.x] = incl;
+  if (tid == 0) counts[blockIdx.x] = carry;
 }
 
 // Prefill path, kernel 3: scatter every entry to its expert-major position.
 __global__ __launch_bounds__(BLOCK) void scatter_kernel(
     const int32_t *__restrict__ packed, const int32_t *__restrict__ tile_rank,
     const int32_t *__restrict__ hist, int ntiles, const int32_t *__restrict__ counts, int e_out,
-    int64_t n, int K, int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
-    int32_t *__restrict__ inv) {
+    int64_t n, int K, int tile_tokens, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ perm, int32_t *__restrict__ inv) {
   __shared__ int32_t offs[MOE_ROUTE_MAX_EXPERTS + 1];
   __shared__ int32_t wave_tot[WAVES_PER_BLOCK];
   block_exclusive_scan(counts, e_out, offs, wave_tot);
@@ -207,7 +231,7 @@ __global__ __launch_bounds__(BLOCK) void scatter_kernel(
   for (int64_t f = (int64_t)blockIdx.x * BLOCK + threadIdx.x; f < n;
        f += (int64_t)gridDim.x * BLOCK) {
     const int e = packed[f] >> 16;
-    const int tile = (int)((f / K) / TILE_TOKENS);
+    const int tile = (int)((f / K) / tile_tokens);
     const int pos = offs[e] + hist[(size_t)e * ntiles + tile] + tile_rank[f];
     perm[pos] = (int32_t)f;
     if (inv) inv[f] = pos;
@@ -219,7 +243,7 @@ __global__ void sigmoid_kernel(const float *__restrict__ x, float *__restrict__ 
                                int mode) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x)
-    y[i] = mode == 1 ? sigmoid_rn32_dd(x[i]) : sigmoid_rn32(x[i]);
+    y[i] = mode == 1 ? sigmoid_rn32_dd(x[i]) : (mode == 2 ? fast_sigmoid(x[i]) : sigmoid_rn32(x[i]));
 }
 
 // ---------------------------------------------------------------------------
@@ -279,17 +303,18 @@ static hipError_t launch_route(const float *logits, const float *bias, int T, co
   int32_t *tile_rank = reinterpret_cast<int32_t *>(
       ws + CONTROL_BYTES + align256((size_t)rp.e_out * ntiles * sizeof(int32_t)));
   const int cus = cu_count();
-  const int grid1 = ntiles < 4 * cus ? ntiles : 4 * cus;
   if (g_ev_before) hipEventRecord(g_ev_before, st);
-  route_tiles_kernel<NP><<<grid1, BLOCK, 0, st>>>(logits, bias, T, rp, ntiles, o->topk_ids,
-                                                   o->topk_weights, o->packed, hist, tile_rank);
+  route_tiles_kernel<NP><<<ntiles, TILE_BLOCK, 0, st>>>(logits, bias, T, rp, o->topk_ids,
+                                                         o->topk_weights, o->packed, hist, ntiles,
+                                                         tile_rank);
   if (g_ev_after) hipEventRecord(g_ev_after, st);
-  tile_prefix_kernel<<<rp.e_out, 64, 0, st>>>(hist, ntiles, o->counts);
+  tile_prefix_kernel<<<rp.e_out, BLOCK, 0, st>>>(hist, ntiles, o->counts);
   const int64_t n = (int64_t)T * rp.K;
   int64_t g3 = (n + BLOCK * 4 - 1) / (BLOCK * 4);
   if (g3 > 8 * cus) g3 = 8 * cus;
   scatter_kernel<<<(int)g3, BLOCK, 0, st>>>(o->packed, tile_rank, hist, ntiles, o->counts,
-                                            rp.e_out, n, rp.K, o->offsets, o->perm, o->inv_perm);
+                                            rp.e_out, n, rp.K, TILE_TOKENS, o->offsets,
+                                            o->perm, o->inv_perm);
   return hipGetLastError();
 }
 
@@ -415,6 +440,18 @@ int moe_route_local(const float *logits, const float *bias, int32_t num_tokens,
                          num_local_experts, out, workspace, workspace_bytes, stream);
 }
 
+int64_t moe_route_exact_path_tokens(int32_t reset) {
+  unsigned long long v = 0;
+  if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(moe::g_exact_path_tokens), sizeof(v)) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (reset) {
+    const unsigned long long z = 0;
+    if (hipMemcpyToSymbol(HIP_SYMBOL(moe::g_exact_path_tokens), &z, sizeof(z)) != hipSuccess)
+      return MOE_ERR_HIP;
+  }
+  return (int64_t)v;
+}
+
 int moe_route_set_kernel_events(void *before, void *after) {
   if ((before == nullptr) != (after == nullptr)) return MOE_ERR_NULL;
   moe::g_ev_before = reinterpret_cast<hipEvent_t>(before);
@@ -426,7 +463,7 @@ int moe_sigmoid_rn32(const float *x, float *y, int64_t n, int32_t mode, void *st
   if (n < 0) return MOE_ERR_SHAPE;
   if (n == 0) return MOE_OK;
   if (!x || !y) return MOE_ERR_NULL;
-  if (mode != 0 && mode != 1) return MOE_ERR_UNSUPPORTED;
+  if (mode < 0 || mode > 2) return MOE_ERR_UNSUPPORTED;
   int64_t grid = (n + 255) / 256;
   if (grid > 65536) grid = 65536;
   moe::sigmoid_kernel<<<(int)grid, 256, 0, reinterpret_cast<hipStream_t>(stream)>>>(x, y, n, mode);

@@ -1,11 +1,11 @@
 // route_wave.hpp - one wavefront routes one token (gfx950, wave64).
 //
-// Steps, in the order of the method (a sigmoid router with a correction bias
-// and a grouped top-k: "[ROCm][Perf] Kimi-K3: token-sharded residual stream
-// for long prefills", author's reply on shard-routed test coverage; packed
-// ids and the rank-local pack epilogue: "[kimi-k3] Rank-local expert ids for
-// the EP routed MoE (upstream #45544)", commit message):
-//   s  = RN32(sigma(logit))                 (exact, rn_sigmoid.hpp)
+// The method (a sigmoid router with a correction bias and a grouped top-k:
+// "[ROCm][Perf] Kimi-K3: token-sharded residual stream for long prefills",
+// author's reply on shard-routed test coverage; packed ids and the
+// rank-local pack epilogue: "[kimi-k3] Rank-local expert ids for the EP
+// routed MoE (upstream #45544)", commit message):
+//   s  = RN32(sigma(logit))                 exact binary32 (rn_sigmoid.hpp)
 //   sp = fl32(s + bias)                      selection key only
 //   group score = fl32 sum of the group's top `group_topn` sp
 //   keep the topk_group best groups          ties -> lower group index
@@ -13,11 +13,25 @@
 //   w_k = s_k / sum_j s_j                    binary64, rounded to binary32
 //   packed = (id' << 16) | bf16_rne(w)       id' = rank-local id if relabelled
 //
+// Two ways to the same answer:
+//  * route_token_fast: every score is first approximated with the hardware
+//    exp2/rcp (error <= FAST_SIG_ERR, checked exhaustively over all binary32
+//    inputs by a GPU test). The group choice is accepted only when the score
+//    margin between the kept and the dropped groups exceeds the error bound.
+//    A threshold, found by bisection on the lanes' top-2 pool, picks a small
+//    candidate set that holds every possible winner; the candidates are then
+//    scored EXACTLY and ranked by exact (sp, id). The result is accepted only
+//    when the exact top_k-th score beats the largest score any non-candidate
+//    can have. Otherwise the token takes
+//  * route_token_exact: exact scores for all experts, exact group scores,
+//    top_k by wave argmax.
+//
 // Lane layout. Lane l belongs to group g = l / LPG (LPG = 64 / G lanes per
 // group) and holds 2*NP experts of that group as NP float2 pairs:
 //   e(i, j) = g*Eg + 2*(l % LPG) + 2*LPG*i + j,   i < NP, j < 2,
 // so every load instruction of the wave reads 8-byte pieces that tile whole
 // 64-byte segments, and group reductions stay inside LPG adjacent lanes.
+// Slot q = 2i + j: within a lane, expert ids increase with the slot.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -26,6 +40,8 @@
 #include "rn_sigmoid.hpp"
 
 namespace moe {
+
+constexpr int kMaxTopK = 32;
 
 struct RouteParams {
   int E;          // experts
@@ -41,6 +57,95 @@ struct RouteParams {
   int e_out;      // output id space
 };
 
+// Tokens that took the exact path (diagnostic, moe_route_exact_path_tokens).
+__device__ unsigned long long g_exact_path_tokens = 0ull;
+
+// Per-wave LDS scratch of the fast path.
+struct WaveScratch {
+  uint32_t cand[64];              // candidates: expert id
+  unsigned long long key[64];     // exact keys of the candidates
+  uint2 res[kMaxTopK];            // selected, by slot: (expert id, s bits)
+};
+
+// ---------------------------------------------------------------------------
+// Cross-lane helpers (gfx9 DPP controls)
+// ---------------------------------------------------------------------------
+constexpr int DPP_XOR1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141; // lane i <-> 7-i within 8
+constexpr int DPP_MIRROR = 0x140;      // lane i <-> 15-i within 16
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = dpp<CTRL>((uint32_t)u), hi = dpp<CTRL>((uint32_t)(u >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint32_t umin(uint32_t a, uint32_t b) { return a < b ? a : b; }
+__device__ __forceinline__ uint32_t umed3(uint32_t a, uint32_t b, uint32_t c) {
+  return umax(umin(a, b), umin(umax(a, b), c));
+}
+
+__device__ __forceinline__ uint32_t readlane_u32(uint32_t v, int l) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+
+// Maximum / minimum over the 64 lanes (wave-uniform result).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = umax(v, dpp<DPP_XOR1>(v));
+  v = umax(v, dpp<DPP_XOR2>(v));
+  v = umax(v, dpp<DPP_HALF_MIRROR>(v));
+  v = umax(v, dpp<DPP_MIRROR>(v));
+  return umax(umax(readlane_u32(v, 0), readlane_u32(v, 16)),
+              umax(readlane_u32(v, 32), readlane_u32(v, 48)));
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = umin(v, dpp<DPP_XOR1>(v));
+  v = umin(v, dpp<DPP_XOR2>(v));
+  v = umin(v, dpp<DPP_HALF_MIRROR>(v));
+  v = umin(v, dpp<DPP_MIRROR>(v));
+  return umin(umin(readlane_u32(v, 0), readlane_u32(v, 16)),
+              umin(readlane_u32(v, 32), readlane_u32(v, 48)));
+}
+
+// Merge the top-2 (with multiplicity) of two disjoint sets.
+__device__ __forceinline__ void top2_merge(uint32_t &a1, uint32_t &a2, uint32_t b1, uint32_t b2) {
+  const uint32_t n2 = umax(umin(a1, b1), umax(a2, b2));
+  a1 = umax(a1, b1);
+  a2 = n2;
+}
+
+// Top-2 over each aligned run of `lpg` lanes (all lanes of the run get it).
+__device__ __forceinline__ void group_top2(uint32_t &m1, uint32_t &m2, int lpg) {
+  if (lpg >= 2) top2_merge(m1, m2, dpp<DPP_XOR1>(m1), dpp<DPP_XOR1>(m2));
+  if (lpg >= 4) top2_merge(m1, m2, dpp<DPP_XOR2>(m1), dpp<DPP_XOR2>(m2));
+  if (lpg >= 8) top2_merge(m1, m2, dpp<DPP_HALF_MIRROR>(m1), dpp<DPP_HALF_MIRROR>(m2));
+  if (lpg >= 16) top2_merge(m1, m2, dpp<DPP_MIRROR>(m1), dpp<DPP_MIRROR>(m2));
+  if (lpg >= 32) top2_merge(m1, m2, __shfl_xor(m1, 16), __shfl_xor(m2, 16));
+  if (lpg >= 64) top2_merge(m1, m2, __shfl_xor(m1, 32), __shfl_xor(m2, 32));
+}
+
+__device__ __forceinline__ int mbcnt(uint64_t mask) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// LDS written by some lanes of the wave is read by others: LDS instructions
+// of one wavefront execute in order; keep the compiler from reordering.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Monotone map of finite binary32 values to unsigned integers.
 __device__ __forceinline__ uint32_t ord_f32(float v) {
   const uint32_t u = __float_as_uint(v);
@@ -54,7 +159,35 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float w) {
 
 __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
-// Bias in the lane layout (loaded once per wave, reused for every token).
+// ---------------------------------------------------------------------------
+// Approximate scores
+// ---------------------------------------------------------------------------
+// Bound on |fast_sigmoid(x) - RN32(sigma(x))| over all finite binary32 x.
+constexpr float FAST_SIG_ERR = 0x1p-20f;
+
+__device__ __forceinline__ float fast_sigmoid(float x) {
+  const float e = __builtin_amdgcn_exp2f(x * -1.44269504088896340736f);
+  return __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// Approximate key: the bits of max(sp~, 0) with the low 4 bits replaced by
+// (15 - slot). Keys order by value (to 16 ulp), then by lower expert id
+// within a lane. key_value() gives the value part.
+__device__ __forceinline__ uint32_t approx_key(float sp, int slot) {
+  const int b = __float_as_int(sp);
+  return ((uint32_t)(b > 0 ? b : 0) & 0xFFFFFFF0u) | (uint32_t)(15 - slot);
+}
+__device__ __forceinline__ float key_value(uint32_t k) { return __uint_as_float(k & 0xFFFFFFF0u); }
+
+// |key_value(key_e) - sp_e| <= err_bound(key_value(key_e)) for every expert
+// whose key is not clamped: the approximation error, two binary32 roundings
+// (of s~ + b and of s + b) and the 15-ulp truncation, with margin.
+__device__ __forceinline__ float err_bound(float v) { return 1.01f * FAST_SIG_ERR + 0x1p-18f * v; }
+// Same for a group score of up to two terms plus its own rounding.
+__device__ __forceinline__ float group_err_bound(float v) {
+  return 2.02f * FAST_SIG_ERR + 0x1p-17f * v;
+}
+
 template <int NP>
 __device__ __forceinline__ void load_lane_layout(const float *__restrict__ v, const RouteParams &p,
                                                  int lane, float (&out)[2 * NP]) {
@@ -69,44 +202,170 @@ __device__ __forceinline__ void load_lane_layout(const float *__restrict__ v, co
   }
 }
 
-// Routes token t (row = logits + t*E). Lanes 0..K-1 write slot k = lane of
-// topk_ids / topk_weights / packed and return the output id id'; other lanes
-// return -1. Must be called by all 64 lanes of the wave.
+__device__ __forceinline__ int slot_expert(int e0, int lpg, int q) {
+  return e0 + 2 * lpg * (q >> 1) + (q & 1);
+}
+
+// ---------------------------------------------------------------------------
+// Fast path. Returns true (and the selection in lanes 0..K-1) only when the
+// result is proven equal to the exact one.
+// ---------------------------------------------------------------------------
 template <int NP>
-__device__ __forceinline__ int route_token_wave(const float *__restrict__ row,
-                                                const float (&bias)[2 * NP],
-                                                const RouteParams &p, int lane, int64_t t,
-                                                int32_t *__restrict__ ids,
-                                                float *__restrict__ wts,
-                                                int32_t *__restrict__ packed) {
+__device__ __forceinline__ bool route_token_fast(const float *__restrict__ row,
+                                                 const float (&x)[2 * NP],
+                                                 const float (&bias)[2 * NP],
+                                                 const float *__restrict__ bias_g,
+                                                 const RouteParams &p, int lane,
+                                                 WaveScratch *L, int &my_id, float &my_s) {
   constexpr int M = 2 * NP;
-  float x[M];
-  load_lane_layout<NP>(row, p, lane, x);
+  const int g = lane >> p.lpg_log2;
+  const int e0 = g * p.eg + 2 * (lane & (p.lpg - 1));
+
+  uint32_t key[M];
+#pragma unroll
+  for (int q = 0; q < M; ++q) key[q] = approx_key(fast_sigmoid(x[q]) + bias[q], q);
+
+  // lane top-2 keys, then the group's top-2
+  uint32_t p1 = 0u, p2 = 0u;
+#pragma unroll
+  for (int q = 0; q < M; ++q) {
+    p2 = umed3(p1, p2, key[q]);
+    p1 = umax(p1, key[q]);
+  }
+  uint32_t g1 = p1, g2 = p2;
+  group_top2(g1, g2, p.lpg);
+  const uint32_t glast = (p.topn == 2) ? g2 : g1;
+  const float gs = (p.topn == 2) ? key_value(g1) + key_value(g2) : key_value(g1);  // >= 0
+
+  // group rank by approximate score; equal scores do not outrank each other,
+  // so a tie at the cut yields more than TG kept groups and is rejected
+  int rank = 0;
+  for (int gg = 0; gg < p.G; ++gg) {
+    const float o = __uint_as_float(readlane_u32(__float_as_uint(gs), gg << p.lpg_log2));
+    rank += (o > gs) ? 1 : 0;
+  }
+  const bool kept = rank < p.TG;
+  if (p.TG < p.G) {
+    if (__popcll(__ballot(kept)) != (unsigned)(p.TG * p.lpg)) return false;
+    const uint32_t gsb = __float_as_uint(gs);
+    const float kmin = __uint_as_float(wave_min_u32(kept ? gsb : 0x7F7FFFFFu));
+    const float dmax = __uint_as_float(wave_max_u32(kept ? 0u : gsb));
+    if (!(kmin - group_err_bound(kmin) > dmax + group_err_bound(dmax))) return false;
+  }
+  // the kept groups' scores must rest on unclamped (positive) values
+  if (__ballot(kept && (glast & 0xFFFFFFF0u) == 0u)) return false;
+
+  // threshold: bisection on the kept lanes' top-2 pool
+  const uint32_t q1 = kept ? p1 : 0u, q2 = kept ? p2 : 0u;
+  const int need = p.K + 2;
+  uint32_t lo = 1u;
+  const int c0 = __popcll(__ballot(q1 >= 1u)) + __popcll(__ballot(q2 >= 1u));
+  if (c0 >= need) {
+    // every kept lane has both pool keys >= its own p2: start at the smallest
+    lo = wave_min_u32(kept ? q2 : 0xFFFFFFFFu);
+    uint32_t hi = wave_max_u32(q1) + 1u;
+    while (hi - lo > 1u) {
+      const uint32_t mid = lo + ((hi - lo) >> 1);
+      const int c = __popcll(__ballot(q1 >= mid)) + __popcll(__ballot(q2 >= mid));
+      if (c >= need) {
+        lo = mid;
+        if (c <= 32) break;
+      } else {
+        hi = mid;
+      }
+    }
+  }
+  const uint32_t theta = lo;
+
+  // compact every kept expert whose key reaches the threshold
+  int m = 0;
+#pragma unroll
+  for (int q = 0; q < M; ++q) {
+    const bool pr = kept && key[q] >= theta;
+    const uint64_t bm = __ballot(pr);
+    if (bm) {
+      const int pos = m + mbcnt(bm);
+      if (pr && pos < 64) L->cand[pos] = (uint32_t)slot_expert(e0, p.lpg, q);
+      m += __popcll(bm);
+    }
+  }
+  if (m > 64 || m < p.K) return false;
+  wave_lds_sync();
+
+  // exact scores and exact ranks of the candidates
+  unsigned long long ek = 0ull;
+  float es = 0.0f, esp = 0.0f;
+  uint32_t eid = 0u;
+  const bool is_cand = lane < m;
+  if (is_cand) {
+    eid = L->cand[lane];
+    es = sigmoid_rn32(row[eid]);
+    esp = es + bias_g[eid];
+    ek = ((unsigned long long)ord_f32(esp) << 32) | (unsigned long long)(~eid);
+    L->key[lane] = ek;
+  }
+  wave_lds_sync();
+  int r = 0;
+  if (is_cand) {
+    // keys beyond m were never written this token: pad to a multiple of 4
+    // with zeros (below every candidate key)
+    for (int j = m; j < ((m + 3) & ~3); ++j) L->key[j] = 0ull;
+  }
+  wave_lds_sync();
+  if (is_cand) {
+    for (int j = 0; j < m; j += 4) {
+      const unsigned long long k0 = L->key[j], k1 = L->key[j + 1], k2 = L->key[j + 2],
+                               k3 = L->key[j + 3];
+      r += (k0 > ek ? 1 : 0) + (k1 > ek ? 1 : 0) + (k2 > ek ? 1 : 0) + (k3 > ek ? 1 : 0);
+    }
+  }
+  if (is_cand && r < p.K) L->res[r] = make_uint2(eid, __float_as_uint(es));
+  const uint64_t bk = __ballot(is_cand && r == p.K - 1);
+  const int kl = (int)__ffsll((unsigned long long)bk) - 1;
+  const float cK = __uint_as_float(readlane_u32(__float_as_uint(esp), kl));
+  // no non-candidate (key < theta) can reach the exact K-th score
+  const float tau = key_value(theta);
+  if (!(cK > tau + err_bound(tau))) return false;
+  wave_lds_sync();
+  if (lane < p.K) {
+    const uint2 rr = L->res[lane];
+    my_id = (int)rr.x;
+    my_s = __uint_as_float(rr.y);
+  }
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// Exact path (every score exact; top-k by wave argmax).
+// ---------------------------------------------------------------------------
+template <int NP>
+__device__ __forceinline__ void route_token_exact(const float *__restrict__ row,
+                                               const float (&x)[2 * NP],
+                                               const float (&bias)[2 * NP],
+                                               const RouteParams &p, int lane, int &my_id,
+                                               float &my_s) {
+  constexpr int M = 2 * NP;
   const int g = lane >> p.lpg_log2;
   const int e0 = g * p.eg + 2 * (lane & (p.lpg - 1));
 
   float sp[M];
 #pragma unroll
-  for (int j = 0; j < M; ++j) sp[j] = sigmoid_rn32(x[j]) + bias[j];
+  for (int q = 0; q < M; ++q) sp[q] = sigmoid_rn32(x[q]) + bias[q];
 
-  // Top two biased scores of the group, with multiplicity.
   float m1 = -__builtin_inff(), m2 = -__builtin_inff();
 #pragma unroll
-  for (int j = 0; j < M; ++j) {
-    m2 = fmaxf(m2, fminf(m1, sp[j]));
-    m1 = fmaxf(m1, sp[j]);
+  for (int q = 0; q < M; ++q) {
+    m2 = fmaxf(m2, fminf(m1, sp[q]));
+    m1 = fmaxf(m1, sp[q]);
   }
   for (int d = 1; d < p.lpg; d <<= 1) {
-    const float q1 = __shfl_xor(m1, d);
-    const float q2 = __shfl_xor(m2, d);
-    const float n2 = fmaxf(fminf(m1, q1), fmaxf(m2, q2));
-    m1 = fmaxf(m1, q1);
+    const float o1 = __shfl_xor(m1, d);
+    const float o2 = __shfl_xor(m2, d);
+    const float n2 = fmaxf(fminf(m1, o1), fmaxf(m2, o2));
+    m1 = fmaxf(m1, o1);
     m2 = n2;
   }
   const float gs = (p.topn == 2) ? (m1 + m2) : m1;
-
-  // Rank of this lane's group: groups with a larger score, or an equal score
-  // and a lower index, come first.
   int rank = 0;
   for (int gg = 0; gg < p.G; ++gg) {
     const float o = __shfl(gs, gg << p.lpg_log2);
@@ -114,39 +373,46 @@ __device__ __forceinline__ int route_token_wave(const float *__restrict__ row,
   }
   const bool kept = rank < p.TG;
 
-  // Key: ordered sp in the high word, ~id in the low word, so the maximum
-  // key is the best (sp desc, id asc) candidate. Dropped groups get 0.
-  uint64_t key[M];
-#pragma unroll
-  for (int i = 0; i < NP; ++i) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint32_t e = (uint32_t)(e0 + 2 * p.lpg * i + j);
-      key[2 * i + j] = kept ? (((uint64_t)ord_f32(sp[2 * i + j]) << 32) | (uint64_t)(~e)) : 0ull;
-    }
-  }
-  int my_id = 0;
+  // top-k by wave argmax over (sp desc, id asc); keys are built on the fly
+  // from sp and the slot, and a per-lane bitmask marks slots already taken
+  uint32_t taken = kept ? 0u : 0xFFFFFFFFu;
+  my_id = 0;
   for (int r = 0; r < p.K; ++r) {
     uint64_t best = 0;
 #pragma unroll
-    for (int j = 0; j < M; ++j) best = umax64(best, key[j]);
+    for (int q = 0; q < M; ++q) {
+      const uint32_t e = (uint32_t)slot_expert(e0, p.lpg, q);
+      const uint64_t k = ((uint64_t)ord_f32(sp[q]) << 32) | (uint64_t)(~e);
+      best = ((taken >> q) & 1u) ? best : umax64(best, k);
+    }
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) best = umax64(best, __shfl_xor(best, d));
-    if (lane == r) my_id = (int)(~(uint32_t)best);
+    const uint32_t win = ~(uint32_t)best;
+    if (lane == r) my_id = (int)win;
 #pragma unroll
-    for (int j = 0; j < M; ++j) key[j] = (key[j] == best) ? 0ull : key[j];
+    for (int q = 0; q < M; ++q)
+      if ((uint32_t)slot_expert(e0, p.lpg, q) == win) taken |= 1u << q;
   }
+  my_s = (lane < p.K) ? sigmoid_rn32(row[my_id]) : 0.0f;
+}
 
-  // Weights: unbiased s of the selected experts over their binary64 sum.
-  float s_sel = 0.0f;
-  if (lane < p.K) s_sel = sigmoid_rn32(row[my_id]);
-  double sum = (lane < p.K) ? (double)s_sel : 0.0;
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) sum += __shfl_xor(sum, d);
-
+// ---------------------------------------------------------------------------
+// Epilogue: weights, relabel, pack, store. Lanes 0..K-1 hold (id, s) of
+// slot k = lane. Returns the output id of the lane's slot (-1 for k >= K).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int route_epilogue(int my_id, float my_s, const RouteParams &p,
+                                              int lane, int64_t t, int32_t *__restrict__ ids,
+                                              float *__restrict__ wts,
+                                              int32_t *__restrict__ packed) {
+  double sum = (lane < p.K) ? (double)my_s : 0.0;
+  sum += dpp_f64<DPP_XOR1>(sum);
+  sum += dpp_f64<DPP_XOR2>(sum);
+  sum += dpp_f64<DPP_HALF_MIRROR>(sum);
+  sum += dpp_f64<DPP_MIRROR>(sum);            // lanes 0..15 hold the row sum
+  if (p.K > 16) sum += __shfl_xor(sum, 16);   // rows 0 and 1
   int idp = -1;
   if (lane < p.K) {
-    const float w = (float)((double)s_sel / sum);
+    const float w = (float)((double)my_s / sum);
     idp = my_id;
     if (p.local) idp = (my_id >= p.off && my_id < p.off + p.cnt) ? my_id - p.off : p.cnt + lane;
     const size_t o = (size_t)t * p.K + lane;
@@ -155,6 +421,28 @@ __device__ __forceinline__ int route_token_wave(const float *__restrict__ row,
     packed[o] = (int32_t)(((uint32_t)idp << 16) | bf16_rne_bits(w));
   }
   return idp;
+}
+
+// Routes token t whose logits are in x (lane layout; row = the token's row).
+template <int NP>
+__device__ __forceinline__ int route_token(const float *__restrict__ row,
+                                           const float (&x)[2 * NP], const float (&bias)[2 * NP],
+                                           const float *__restrict__ bias_g, const RouteParams &p,
+                                           int lane, int64_t t, WaveScratch *L,
+                                           int32_t *__restrict__ ids, float *__restrict__ wts,
+                                           int32_t *__restrict__ packed) {
+  // Lane-derived values (expert ids of the slots, ...) are cheap to
+  // recompute; an opaque copy of the lane index keeps the compiler from
+  // hoisting them out of the caller's token loop into dozens of registers.
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  int my_id = 0;
+  float my_s = 0.0f;
+  if (!route_token_fast<NP>(row, x, bias, bias_g, p, ln, L, my_id, my_s)) {
+    if (ln == 0) atomicAdd(&g_exact_path_tokens, 1ull);
+    route_token_exact<NP>(row, x, bias, p, ln, my_id, my_s);
+  }
+  return route_epilogue(my_id, my_s, p, ln, t, ids, wts, packed);
 }
 
 }  // namespace moe

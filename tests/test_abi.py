@@ -136,7 +136,7 @@ def test_router_gemm_validation(L):
 def test_sigmoid_validation(L):
     assert L.moe_sigmoid_rn32(FAKE, FAKE, -1, 0, None) == ERR_SHAPE
     assert L.moe_sigmoid_rn32(None, FAKE, 5, 0, None) == ERR_NULL
-    assert L.moe_sigmoid_rn32(FAKE, FAKE, 5, 2, None) == ERR_UNSUP
+    assert L.moe_sigmoid_rn32(FAKE, FAKE, 5, 3, None) == ERR_UNSUP  # invalid mode: no launch
     assert L.moe_sigmoid_rn32(FAKE, FAKE, 0, 0, None) == OK
 
 

@@ -219,3 +219,54 @@ def test_global_and_local_entries_reach_the_gemm_in_the_same_order():
     assert entries(loc, 0, cnt, off) == entries(g, off, off + cnt, 0)
     assert np.array_equal(g["topk_ids"], loc["topk_ids"])
     assert np.array_equal(g["packed"] & 0xFFFF, loc["packed"] & 0xFFFF)
+
+
+# --------------------------------------------------------------------------
+# the fast path's error bound and its fallback
+# --------------------------------------------------------------------------
+
+def _kernel_fast_sig_err():
+    import os
+    import re
+    src = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                       "moe_expert_routing_amd", "csrc", "route_wave.hpp")
+    m = re.search(r"FAST_SIG_ERR\s*=\s*0x1p-(\d+)f", open(src).read())
+    return 2.0 ** -int(m.group(1))
+
+
+def test_fast_sigmoid_error_bound_exhaustive():
+    """Every finite binary32 input: |fast approximation - exact| must stay
+    below half the bound the kernels certify against."""
+    bound = _kernel_fast_sig_err()
+    worst, worst_x = 0.0, None
+    chunk = 1 << 26
+    say(f"fast sigmoid sweep of 2^32 inputs, bound {bound:.3g}")
+    for c in range((1 << 32) // chunk):
+        bits = torch.arange(c * chunk, (c + 1) * chunk, dtype=torch.int64, device=DEV)
+        bits = torch.where(bits >= (1 << 31), bits - (1 << 32), bits).to(torch.int32)
+        x = bits.view(torch.float32)
+        x = torch.where(torch.isfinite(x), x, torch.zeros_like(x))
+        exact = M.sigmoid_rn32(x, mode=0)
+        fast = M.sigmoid_rn32(x, mode=2)
+        err = (fast.double() - exact.double()).abs()
+        i = int(torch.argmax(err))
+        e = float(err[i])
+        if e > worst:
+            worst, worst_x = e, float(x[i])
+    say(f"worst |fast - exact| = {worst:.4g} at x = {worst_x}")
+    assert worst <= bound / 2, (worst, worst_x)
+
+
+def test_both_paths_are_exercised():
+    """Random decode tokens take the fast path; rows whose scores all tie
+    take the exact path; both give the oracle's answer."""
+    c = W.random_case(64, seed=4242, off=112, cnt=112)
+    M.exact_path_tokens(reset=True)
+    assert_parity(run_case(c), oracle_case(c), "random64")
+    n_random = M.exact_path_tokens(reset=True)
+    logits = np.zeros((16, 896), np.float32)
+    c2 = W.RouteCase("all_tied", logits, np.zeros(896, np.float32))
+    assert_parity(run_case(c2), oracle_case(c2), "all_tied")
+    n_tied = M.exact_path_tokens(reset=True)
+    say(f"exact-path tokens: random {n_random}/64, all-tied {n_tied}/16")
+    assert n_random <= 2 and n_tied == 16
