@@ -33,7 +33,7 @@ METRIC = "routing µs/call at 8/16/64 tokens; routed tokens/s + HBM GB/s at 32K 
 HBM_PEAK_GBPS = 8000.0
 BYTES_PER_TOKEN_PATH = 3904     # logits 3584 + ids, weights, packed, perm, inv (5 x 64)
 BYTES_PER_TOKEN_ROUTE_KERNEL = 3776  # logits 3584 + ids, weights, packed (3 x 64)
-PROFILE_PMC = os.path.join(ROOT, "profiles", "pmc_route_tiles_long_prefill_32768.txt")
+PROFILE_PMC = os.path.join(ROOT, "profiles", "pmc_route_tokens_long_prefill_32768.txt")
 
 
 def log(msg: str) -> None:
@@ -290,7 +290,7 @@ def main():
         "decode_us_per_call": decode,
         "decode_us_per_call_hipgraph": decode_graph,
         "router_gemm_route": gemm,
-        "roofline": {"bound": "hbm", "kernel": "route_tiles_kernel",
+        "roofline": {"bound": "hbm", "kernel": "route_tokens_kernel",
                      "achieved": round(kern_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(frac, 4),
                      "kernel_us_avg": round(kern_avg_ms * 1e3, 2),

@@ -5,13 +5,14 @@
 //    and publish their outputs; the last block to arrive (ticket in the
 //    workspace control block) builds counts, offsets and the permutation from
 //    per-expert 64-bit token masks in LDS.
-//  * prefill, T > 64: three launches.
-//      route_tiles:  tiles of 64 tokens; each block routes its tiles, keeps a
-//                    64-bit token mask per output id in LDS, and writes the
-//                    tile histogram hist[e'][tile] and each entry's rank
-//                    among the tile's entries of the same id.
-//      tile_prefix:  one wave per output id: exclusive scan of hist[e'][:]
-//                    over tiles, total -> counts[e'].
+//  * prefill, T > 64: four launches.
+//      route_tokens: one token per wave, waves independent (no barriers), so
+//                    the per-token latency is hidden by occupancy alone.
+//      tile_count:   tiles of 64 tokens: a 64-bit token mask per output id in
+//                    LDS gives the tile histogram hist[e'][tile] and each
+//                    entry's rank among the tile's entries of the same id.
+//      tile_prefix:  per output id, exclusive scan of hist[e'][:] over tiles;
+//                    total -> counts[e'].
 //      scatter:      offsets = exclusive scan of counts; each entry goes to
 //                    offsets[e'] + hist[e'][tile] + rank_in_tile.
 // Within one token the output ids are distinct (top-k ids are distinct and
@@ -33,11 +34,8 @@ namespace moe {
 constexpr int WAVES_PER_BLOCK = 4;
 constexpr int BLOCK = 64 * WAVES_PER_BLOCK;
 constexpr size_t CONTROL_BYTES = 256;
-// Prefill tiles: one block of 16 waves routes 16 tokens, one per wave (no
-// token loop: the per-token code keeps its registers low enough for eight
-// waves per SIMD).
-constexpr int TILE_TOKENS = 16;
-constexpr int TILE_BLOCK = 64 * TILE_TOKENS;
+// Prefill tiles of the permutation: 64 tokens (token masks are 64-bit).
+constexpr int TILE_TOKENS = 64;
 
 // Exclusive scan of in[0..n) (n <= 1024, any memory) into out[0..n] in LDS,
 // out[n] = total. All BLOCK threads must call it.
@@ -135,40 +133,42 @@ __global__ __launch_bounds__(BLOCK) void route_decode_kernel(
 // Prefill path, kernel 1: route tiles of 64 tokens.
 // ---------------------------------------------------------------------------
 template <int NP>
-__global__ __launch_bounds__(TILE_BLOCK) void route_tiles_kernel(
+__global__ __launch_bounds__(BLOCK) void route_tokens_kernel(
     const float *__restrict__ logits, const float *__restrict__ bias, int T, RouteParams p,
-    int32_t *__restrict__ ids, float *__restrict__ wts, int32_t *__restrict__ packed,
-    int32_t *__restrict__ hist, int ntiles, int32_t *__restrict__ tile_rank) {
-  __shared__ uint32_t mask[MOE_ROUTE_MAX_EXPERTS];  // bit w: token w of the tile
-  __shared__ int16_t idp_sh[TILE_TOKENS][MOE_ROUTE_MAX_TOPK];
-  __shared__ WaveScratch scratch[TILE_TOKENS];
+    int32_t *__restrict__ ids, float *__restrict__ wts, int32_t *__restrict__ packed) {
+  __shared__ WaveScratch scratch[WAVES_PER_BLOCK];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int t = blockIdx.x * WAVES_PER_BLOCK + wave;
+  if (t >= T) return;
+  const float *row = logits + (size_t)t * p.E;
+  float b[2 * NP], x[2 * NP];
+  load_lane_layout<NP>(row, p, lane, x);
+  load_lane_layout<NP>(bias, p, lane, b);
+  route_token<NP>(row, x, b, bias, p, lane, t, &scratch[wave], ids, wts, packed);
+}
+
+// Prefill path, kernel 1b: per tile of TILE_TOKENS tokens, a 64-bit token
+// mask per output id (in LDS) gives the tile histogram hist[e'][tile] and
+// each entry's rank among the tile's entries of the same id.
+__global__ __launch_bounds__(BLOCK) void tile_count_kernel(const int32_t *__restrict__ packed,
+                                                           int T, int K, int e_out,
+                                                           int32_t *__restrict__ hist, int ntiles,
+                                                           int32_t *__restrict__ tile_rank) {
+  __shared__ unsigned long long mask[MOE_ROUTE_MAX_EXPERTS];
   const int tile = blockIdx.x;
-  const int t = tile * TILE_TOKENS + wave;
-  for (int i = threadIdx.x; i < p.e_out; i += TILE_BLOCK) mask[i] = 0u;
-  __syncthreads();
-  if (t < T) {
-    const float *row = logits + (size_t)t * p.E;
-    float b[2 * NP], x[2 * NP];
-    load_lane_layout<NP>(row, p, lane, x);
-    load_lane_layout<NP>(bias, p, lane, b);
-    const int idp = route_token<NP>(row, x, b, bias, p, lane, t, &scratch[wave], ids, wts, packed);
-    if (lane < p.K) {
-      atomicOr(&mask[idp], 1u << wave);
-      idp_sh[wave][lane] = (int16_t)idp;
-    }
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < p.e_out; i += TILE_BLOCK)
-    hist[(size_t)i * ntiles + tile] = __popc(mask[i]);
-  // rank of each entry among the tile's entries with the same output id
   const int nt = min(TILE_TOKENS, T - tile * TILE_TOKENS);
-  for (int q = threadIdx.x; q < nt * p.K; q += TILE_BLOCK) {
-    const int tl = q / p.K, k = q - tl * p.K;
-    tile_rank[((size_t)tile * TILE_TOKENS + tl) * p.K + k] =
-        __popc(mask[idp_sh[tl][k]] & ((1u << tl) - 1u));
-  }
+  const int n = nt * K;
+  const int32_t *pk = packed + (size_t)tile * TILE_TOKENS * K;
+  for (int i = threadIdx.x; i < e_out; i += BLOCK) mask[i] = 0ull;
+  __syncthreads();
+  for (int q = threadIdx.x; q < n; q += BLOCK) atomicOr(&mask[pk[q] >> 16], 1ull << (q / K));
+  __syncthreads();
+  for (int i = threadIdx.x; i < e_out; i += BLOCK)
+    hist[(size_t)i * ntiles + tile] = __popcll(mask[i]);
+  int32_t *tr = tile_rank + (size_t)tile * TILE_TOKENS * K;
+  for (int q = threadIdx.x; q < n; q += BLOCK)
+    tr[q] = __popcll(mask[pk[q] >> 16] & ((1ull << (q / K)) - 1ull));
 }
 
 // Prefill path, kernel 2: per output id, exclusive scan over tiles (in
@@ -303,11 +303,13 @@ static hipError_t launch_route(const float *logits, const float *bias, int T, co
   int32_t *tile_rank = reinterpret_cast<int32_t *>(
       ws + CONTROL_BYTES + align256((size_t)rp.e_out * ntiles * sizeof(int32_t)));
   const int cus = cu_count();
+  const int nblk = (T + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK;
   if (g_ev_before) hipEventRecord(g_ev_before, st);
-  route_tiles_kernel<NP><<<ntiles, TILE_BLOCK, 0, st>>>(logits, bias, T, rp, o->topk_ids,
-                                                         o->topk_weights, o->packed, hist, ntiles,
-                                                         tile_rank);
+  route_tokens_kernel<NP><<<nblk, BLOCK, 0, st>>>(logits, bias, T, rp, o->topk_ids,
+                                                   o->topk_weights, o->packed);
   if (g_ev_after) hipEventRecord(g_ev_after, st);
+  tile_count_kernel<<<ntiles, BLOCK, 0, st>>>(o->packed, T, rp.K, rp.e_out, hist, ntiles,
+                                              tile_rank);
   tile_prefix_kernel<<<rp.e_out, BLOCK, 0, st>>>(hist, ntiles, o->counts);
   const int64_t n = (int64_t)T * rp.K;
   int64_t g3 = (n + BLOCK * 4 - 1) / (BLOCK * 4);

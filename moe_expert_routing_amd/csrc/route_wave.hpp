@@ -13,18 +13,21 @@
 //   w_k = s_k / sum_j s_j                    binary64, rounded to binary32
 //   packed = (id' << 16) | bf16_rne(w)       id' = rank-local id if relabelled
 //
-// Two ways to the same answer:
-//  * route_token_fast: every score is first approximated with the hardware
-//    exp2/rcp (error <= FAST_SIG_ERR, checked exhaustively over all binary32
-//    inputs by a GPU test). The group choice is accepted only when the score
-//    margin between the kept and the dropped groups exceeds the error bound.
-//    A threshold, found by bisection on the lanes' top-2 pool, picks a small
-//    candidate set that holds every possible winner; the candidates are then
-//    scored EXACTLY and ranked by exact (sp, id). The result is accepted only
-//    when the exact top_k-th score beats the largest score any non-candidate
-//    can have. Otherwise the token takes
-//  * route_token_exact: exact scores for all experts, exact group scores,
-//    top_k by wave argmax.
+// How the selection is made exact and fast (select_token):
+//  1. Every score is approximated with the hardware exp2/rcp (error <=
+//     FAST_SIG_ERR, checked over all binary32 inputs by a GPU test) and
+//     turned into a 32-bit key (value bits with the slot in the low 4 bits).
+//  2. The group choice is accepted only when the score margin between the
+//     kept and the dropped groups exceeds the error bound.
+//  3. A threshold, found by bisection on the kept lanes' top-2 keys, picks
+//     a candidate set (<= 64) holding every possible winner; the candidates
+//     are scored EXACTLY and ranked by exact (sp, id).
+//  4. The result is accepted only when the exact top_k-th score beats the
+//     largest score any non-candidate can have.
+// A token that fails a check runs the same pipeline on exact scores (only
+// the key truncation is left to bound), and if that cannot decide either
+// (near-ties within 16 ulp at the threshold), route_token_exact: exact
+// scores, exact group scores, top_k by wave argmax.
 //
 // Lane layout. Lane l belongs to group g = l / LPG (LPG = 64 / G lanes per
 // group) and holds 2*NP experts of that group as NP float2 pairs:
@@ -62,9 +65,9 @@ __device__ unsigned long long g_exact_path_tokens = 0ull;
 
 // Per-wave LDS scratch of the fast path.
 struct WaveScratch {
-  uint32_t cand[64];              // candidates: expert id
-  unsigned long long key[64];     // exact keys of the candidates
-  uint2 res[kMaxTopK];            // selected, by slot: (expert id, s bits)
+  uint32_t cand[64];              // candidate expert ids
+  unsigned long long key[64];     // candidate keys (score, id)
+  uint4 res[kMaxTopK + 1];        // by rank: (id, logit bits, bias bits, score bits)
 };
 
 // ---------------------------------------------------------------------------
@@ -207,66 +210,149 @@ __device__ __forceinline__ int slot_expert(int e0, int lpg, int q) {
 }
 
 // ---------------------------------------------------------------------------
-// Fast path. Returns true (and the selection in lanes 0..K-1) only when the
-// result is proven equal to the exact one.
+// Candidate pipeline
 // ---------------------------------------------------------------------------
-template <int NP>
-__device__ __forceinline__ bool route_token_fast(const float *__restrict__ row,
-                                                 const float (&x)[2 * NP],
-                                                 const float (&bias)[2 * NP],
-                                                 const float *__restrict__ bias_g,
-                                                 const RouteParams &p, int lane,
-                                                 WaveScratch *L, int &my_id, float &my_s) {
+// Descending compare-exchange (wave-uniform operands run on the scalar unit).
+__device__ __forceinline__ void ce_desc(uint32_t &a, uint32_t &b) {
+  const uint32_t hi = umax(a, b), lo = umin(a, b);
+  a = hi;
+  b = lo;
+}
+
+// Sorts 8 values in descending order (19 comparators, depth 6).
+__device__ __forceinline__ void sort8_desc(uint32_t (&v)[8]) {
+  ce_desc(v[0], v[2]); ce_desc(v[1], v[3]); ce_desc(v[4], v[6]); ce_desc(v[5], v[7]);
+  ce_desc(v[0], v[4]); ce_desc(v[1], v[5]); ce_desc(v[2], v[6]); ce_desc(v[3], v[7]);
+  ce_desc(v[0], v[1]); ce_desc(v[2], v[3]); ce_desc(v[4], v[5]); ce_desc(v[6], v[7]);
+  ce_desc(v[2], v[4]); ce_desc(v[3], v[5]);
+  ce_desc(v[1], v[4]); ce_desc(v[3], v[6]);
+  ce_desc(v[1], v[2]); ce_desc(v[3], v[4]); ce_desc(v[5], v[6]);
+}
+
+// |sp~ - sp| for an approximate score of magnitude v: the approximation
+// error plus two binary32 roundings (of s~ + b and of s + b), with margin.
+__device__ __forceinline__ float score_err(float v) {
+  return 1.01f * FAST_SIG_ERR + 0x1p-22f * fabsf(v);
+}
+
+// Selects the top_k experts of one token. The scores that pick the groups
+// and the candidates are the fast approximations (EXACT = false) or the
+// exact scores (EXACT = true). Returns true, with (id, exact s) of slot
+// k = lane in lanes 0..K-1, only when the result is proven equal to the
+// exact selection.
+template <int NP, bool EXACT>
+__device__ __forceinline__ bool select_token(const float *__restrict__ row,
+                                             const float *__restrict__ bias_g,
+                                             const float (&x)[2 * NP], const float (&bias)[2 * NP],
+                                             const RouteParams &p, int lane, WaveScratch *L,
+                                             int &my_id, float &my_s) {
   constexpr int M = 2 * NP;
   const int g = lane >> p.lpg_log2;
   const int e0 = g * p.eg + 2 * (lane & (p.lpg - 1));
 
-  uint32_t key[M];
-#pragma unroll
-  for (int q = 0; q < M; ++q) key[q] = approx_key(fast_sigmoid(x[q]) + bias[q], q);
-
-  // lane top-2 keys, then the group's top-2
-  uint32_t p1 = 0u, p2 = 0u;
+  // ---- streaming: scores -> keys -> the lane's top-4 keys ------------------
+  uint32_t p1 = 0u, p2 = 0u, p3 = 0u, p4 = 0u;
+  float x1 = -__builtin_inff(), x2 = -__builtin_inff();  // exact top-2 (EXACT)
 #pragma unroll
   for (int q = 0; q < M; ++q) {
-    p2 = umed3(p1, p2, key[q]);
-    p1 = umax(p1, key[q]);
+    float sc;
+    if (EXACT) {
+      sc = sigmoid_rn32(x[q]) + bias[q];
+      x2 = fmaxf(x2, fminf(x1, sc));
+      x1 = fmaxf(x1, sc);
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      sc = fast_sigmoid(x[q]) + bias[q];
+    }
+    const uint32_t k = approx_key(sc, q);
+    p4 = umed3(p3, p4, k);
+    p3 = umed3(p2, p3, k);
+    p2 = umed3(p1, p2, k);
+    p1 = umax(p1, k);
   }
-  uint32_t g1 = p1, g2 = p2;
-  group_top2(g1, g2, p.lpg);
-  const uint32_t glast = (p.topn == 2) ? g2 : g1;
-  const float gs = (p.topn == 2) ? key_value(g1) + key_value(g2) : key_value(g1);  // >= 0
 
-  // group rank by approximate score; equal scores do not outrank each other,
-  // so a tie at the cut yields more than TG kept groups and is rejected
-  int rank = 0;
-  for (int gg = 0; gg < p.G; ++gg) {
-    const float o = __uint_as_float(readlane_u32(__float_as_uint(gs), gg << p.lpg_log2));
-    rank += (o > gs) ? 1 : 0;
+  // ---- groups ---------------------------------------------------------------
+  bool kept;
+  uint32_t hi_key;  // one above the largest kept key
+  if (!EXACT && p.G <= 8) {
+    uint32_t g1 = p1, g2 = p2;
+    group_top2(g1, g2, p.lpg);
+    const uint32_t glast = (p.topn == 2) ? g2 : g1;
+    const float gs = (p.topn == 2) ? key_value(g1) + key_value(g2) : key_value(g1);  // >= 0
+    // every group's score and top key, on the scalar unit
+    uint32_t sv[8], top[8];
+#pragma unroll
+    for (int gg = 0; gg < 8; ++gg) {
+      const int src = (gg < p.G ? gg : 0) << p.lpg_log2;
+      sv[gg] = gg < p.G ? readlane_u32(__float_as_uint(gs), src) : 0u;
+      top[gg] = readlane_u32(g1, src);
+    }
+    uint32_t srt[8];
+#pragma unroll
+    for (int gg = 0; gg < 8; ++gg) srt[gg] = sv[gg];
+    sort8_desc(srt);
+    uint32_t keep_thr = srt[0], drop_max = 0u;
+#pragma unroll
+    for (int i = 1; i < 8; ++i) {
+      if (i == p.TG - 1) keep_thr = srt[i];
+      if (i == p.TG) drop_max = srt[i];
+    }
+    if (p.TG < p.G) {
+      const float kmin = __uint_as_float(keep_thr), dmax = __uint_as_float(drop_max);
+      if (!(kmin - group_err_bound(kmin) > dmax + group_err_bound(dmax))) return false;
+    }
+    hi_key = 0u;
+#pragma unroll
+    for (int gg = 0; gg < 8; ++gg)
+      if (gg < p.G && sv[gg] >= keep_thr) hi_key = umax(hi_key, top[gg]);
+    hi_key += 1u;
+    kept = __float_as_uint(gs) >= keep_thr;
+    // the kept groups' scores must rest on unclamped (positive) values
+    if (__ballot(kept && (glast & 0xFFFFFFF0u) == 0u)) return false;
+  } else {
+    // exact group scores (EXACT), or approximate ones with many groups
+    float m1 = EXACT ? x1 : key_value(p1), m2 = EXACT ? x2 : key_value(p2);
+    for (int d = 1; d < p.lpg; d <<= 1) {
+      const float o1 = __shfl_xor(m1, d);
+      const float o2 = __shfl_xor(m2, d);
+      const float n2 = fmaxf(fminf(m1, o1), fmaxf(m2, o2));
+      m1 = fmaxf(m1, o1);
+      m2 = n2;
+    }
+    const float gs = (p.topn == 2) ? (m1 + m2) : m1;
+    int rank = 0;
+    for (int gg = 0; gg < p.G; ++gg) {
+      const float o = __uint_as_float(readlane_u32(__float_as_uint(gs), gg << p.lpg_log2));
+      rank += ((o > gs) || (EXACT && o == gs && gg < g)) ? 1 : 0;
+    }
+    kept = rank < p.TG;
+    if (!EXACT) {
+      if (p.TG < p.G) {
+        if (__popcll(__ballot(kept)) != (unsigned)(p.TG * p.lpg)) return false;
+        const uint32_t gsb = __float_as_uint(gs);
+        const float kmin = __uint_as_float(wave_min_u32(kept ? gsb : 0x7F7FFFFFu));
+        const float dmax = __uint_as_float(wave_max_u32(kept ? 0u : gsb));
+        if (!(kmin - group_err_bound(kmin) > dmax + group_err_bound(dmax))) return false;
+      }
+      if (__ballot(kept && (((p.topn == 2) ? m2 : m1) <= 0.0f))) return false;
+    }
+    hi_key = wave_max_u32(kept ? p1 : 0u) + 1u;
   }
-  const bool kept = rank < p.TG;
-  if (p.TG < p.G) {
-    if (__popcll(__ballot(kept)) != (unsigned)(p.TG * p.lpg)) return false;
-    const uint32_t gsb = __float_as_uint(gs);
-    const float kmin = __uint_as_float(wave_min_u32(kept ? gsb : 0x7F7FFFFFu));
-    const float dmax = __uint_as_float(wave_max_u32(kept ? 0u : gsb));
-    if (!(kmin - group_err_bound(kmin) > dmax + group_err_bound(dmax))) return false;
-  }
-  // the kept groups' scores must rest on unclamped (positive) values
-  if (__ballot(kept && (glast & 0xFFFFFFF0u) == 0u)) return false;
 
-  // threshold: bisection on the kept lanes' top-2 pool
-  const uint32_t q1 = kept ? p1 : 0u, q2 = kept ? p2 : 0u;
+  // ---- threshold: bisection (value space) on the kept lanes' top-4 --------
+  const uint32_t q1 = kept ? p1 : 0u, q2 = kept ? p2 : 0u, q3 = kept ? p3 : 0u,
+                 q4 = kept ? p4 : 0u;
   const int need = p.K + 2;
   uint32_t lo = 1u;
-  const int c0 = __popcll(__ballot(q1 >= 1u)) + __popcll(__ballot(q2 >= 1u));
+  const int c0 = __popcll(__ballot(q1 >= 1u)) + __popcll(__ballot(q2 >= 1u)) +
+                 __popcll(__ballot(q3 >= 1u)) + __popcll(__ballot(q4 >= 1u));
   if (c0 >= need) {
-    // every kept lane has both pool keys >= its own p2: start at the smallest
-    lo = wave_min_u32(kept ? q2 : 0xFFFFFFFFu);
-    uint32_t hi = wave_max_u32(q1) + 1u;
+    uint32_t hi = hi_key;
     while (hi - lo > 1u) {
-      const uint32_t mid = lo + ((hi - lo) >> 1);
-      const int c = __popcll(__ballot(q1 >= mid)) + __popcll(__ballot(q2 >= mid));
+      uint32_t mid = __float_as_uint(0.5f * (key_value(lo) + key_value(hi)));
+      if (mid <= lo || mid >= hi) mid = lo + ((hi - lo) >> 1);
+      const int c = __popcll(__ballot(q1 >= mid)) + __popcll(__ballot(q2 >= mid)) +
+                    __popcll(__ballot(q3 >= mid)) + __popcll(__ballot(q4 >= mid));
       if (c >= need) {
         lo = mid;
         if (c <= 32) break;
@@ -277,60 +363,98 @@ __device__ __forceinline__ bool route_token_fast(const float *__restrict__ row,
   }
   const uint32_t theta = lo;
 
-  // compact every kept expert whose key reaches the threshold
+  // ---- compaction: candidate expert ids ------------------------------------
   int m = 0;
+  if (__ballot(q4 >= theta) == 0ull) {
+    // no lane has more than 3 keys >= theta: the pool holds them all
+    const uint32_t pool[4] = {q1, q2, q3, q4};
+    int base[4];
 #pragma unroll
-  for (int q = 0; q < M; ++q) {
-    const bool pr = kept && key[q] >= theta;
-    const uint64_t bm = __ballot(pr);
-    if (bm) {
-      const int pos = m + mbcnt(bm);
-      if (pr && pos < 64) L->cand[pos] = (uint32_t)slot_expert(e0, p.lpg, q);
-      m += __popcll(bm);
+    for (int i = 0; i < 4; ++i) {
+      base[i] = m;
+      m += __popcll(__ballot(pool[i] >= theta));
+    }
+    if (m > 64) return false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool pr = pool[i] >= theta;
+      const uint64_t bm = __ballot(pr);
+      if (pr) L->cand[base[i] + mbcnt(bm)] = (uint32_t)slot_expert(e0, p.lpg, 15 - (int)(pool[i] & 15u));
+    }
+  } else {
+    // re-scan every slot (keys recomputed)
+    int base[M];
+#pragma unroll
+    for (int q = 0; q < M; ++q) {
+      const float sc = (EXACT ? sigmoid_rn32(x[q]) : fast_sigmoid(x[q])) + bias[q];
+      const uint32_t k = kept ? approx_key(sc, q) : 0u;
+      base[q] = m;
+      m += __popcll(__ballot(k >= theta));
+    }
+    if (m > 64) return false;
+#pragma unroll
+    for (int q = 0; q < M; ++q) {
+      const float sc = (EXACT ? sigmoid_rn32(x[q]) : fast_sigmoid(x[q])) + bias[q];
+      const bool pr = kept && approx_key(sc, q) >= theta;
+      const uint64_t bm = __ballot(pr);
+      if (pr) L->cand[base[q] + mbcnt(bm)] = (uint32_t)slot_expert(e0, p.lpg, q);
     }
   }
-  if (m > 64 || m < p.K) return false;
+  if (m < p.K) return false;
   wave_lds_sync();
 
-  // exact scores and exact ranks of the candidates
-  unsigned long long ek = 0ull;
-  float es = 0.0f, esp = 0.0f;
-  uint32_t eid = 0u;
+  // ---- candidates: scores and ranks by (score desc, id asc) ---------------
   const bool is_cand = lane < m;
+  uint32_t eid = 0u;
+  float cx = 0.0f, cb = 0.0f, csc = 0.0f;
+  uint64_t ck = 0ull;
   if (is_cand) {
     eid = L->cand[lane];
-    es = sigmoid_rn32(row[eid]);
-    esp = es + bias_g[eid];
-    ek = ((unsigned long long)ord_f32(esp) << 32) | (unsigned long long)(~eid);
-    L->key[lane] = ek;
+    cx = row[eid];
+    cb = bias_g[eid];
+    csc = (EXACT ? sigmoid_rn32(cx) : fast_sigmoid(cx)) + cb;
+    ck = ((uint64_t)ord_f32(csc) << 32) | (uint64_t)(~eid);
+    L->key[lane] = ck;
   }
+  if (lane >= m && lane < ((m + 3) & ~3)) L->key[lane] = 0ull;  // pad to a multiple of 4
   wave_lds_sync();
   int r = 0;
   if (is_cand) {
-    // keys beyond m were never written this token: pad to a multiple of 4
-    // with zeros (below every candidate key)
-    for (int j = m; j < ((m + 3) & ~3); ++j) L->key[j] = 0ull;
-  }
-  wave_lds_sync();
-  if (is_cand) {
     for (int j = 0; j < m; j += 4) {
-      const unsigned long long k0 = L->key[j], k1 = L->key[j + 1], k2 = L->key[j + 2],
-                               k3 = L->key[j + 3];
-      r += (k0 > ek ? 1 : 0) + (k1 > ek ? 1 : 0) + (k2 > ek ? 1 : 0) + (k3 > ek ? 1 : 0);
+      const uint64_t k0 = L->key[j], k1 = L->key[j + 1], k2 = L->key[j + 2], k3 = L->key[j + 3];
+      r += (k0 > ck ? 1 : 0) + (k1 > ck ? 1 : 0) + (k2 > ck ? 1 : 0) + (k3 > ck ? 1 : 0);
     }
   }
-  if (is_cand && r < p.K) L->res[r] = make_uint2(eid, __float_as_uint(es));
-  const uint64_t bk = __ballot(is_cand && r == p.K - 1);
-  const int kl = (int)__ffsll((unsigned long long)bk) - 1;
-  const float cK = __uint_as_float(readlane_u32(__float_as_uint(esp), kl));
-  // no non-candidate (key < theta) can reach the exact K-th score
-  const float tau = key_value(theta);
-  if (!(cK > tau + err_bound(tau))) return false;
+  if (is_cand && r <= p.K)
+    L->res[r] = make_uint4(eid, __float_as_uint(cx), __float_as_uint(cb), __float_as_uint(csc));
   wave_lds_sync();
+
+  // ---- certificate -----------------------------------------------------------
+  // slot k = lane for lanes 0..K-1; lane K holds the best non-winner
+  const bool has_next = m > p.K;
+  uint4 rr = make_uint4(0u, 0u, 0u, 0u);
+  if (lane <= p.K && (lane < p.K || has_next)) rr = L->res[lane];
+  const float rsc = __uint_as_float(rr.w);
+  // the K-th score must beat every non-candidate (keys below theta)
+  const float tau = key_value(theta);
+  const float kth = __uint_as_float(readlane_u32(rr.w, p.K - 1));
+  if (EXACT) {
+    if (!(kth > tau + 0x1p-19f * tau)) return false;
+  } else {
+    if (!(kth - score_err(kth) > tau + score_err(tau) + 0x1p-19f * tau)) return false;
+    // adjacent winners (and the K-th vs the best non-winner) must be apart
+    // by more than the error, or be exact twins (same logit and bias)
+    const uint32_t nsc = __shfl_down(rr.w, 1), nx = __shfl_down(rr.y, 1),
+                   nb = __shfl_down(rr.z, 1);
+    const bool check = lane < p.K && (lane < p.K - 1 || has_next);
+    const float nv = __uint_as_float(nsc);
+    const bool sep = (rsc - score_err(rsc)) > (nv + score_err(nv));
+    const bool twin = (rr.y == nx) && (rr.z == nb);
+    if (__ballot(check && !(sep || twin))) return false;
+  }
   if (lane < p.K) {
-    const uint2 rr = L->res[lane];
     my_id = (int)rr.x;
-    my_s = __uint_as_float(rr.y);
+    my_s = sigmoid_rn32(__uint_as_float(rr.y));  // exact score for the weight
   }
   return true;
 }
@@ -438,9 +562,10 @@ __device__ __forceinline__ int route_token(const float *__restrict__ row,
   asm volatile("" : "+v"(ln));
   int my_id = 0;
   float my_s = 0.0f;
-  if (!route_token_fast<NP>(row, x, bias, bias_g, p, ln, L, my_id, my_s)) {
+  if (!select_token<NP, false>(row, bias_g, x, bias, p, ln, L, my_id, my_s)) {
     if (ln == 0) atomicAdd(&g_exact_path_tokens, 1ull);
-    route_token_exact<NP>(row, x, bias, p, ln, my_id, my_s);
+    if (!select_token<NP, true>(row, bias_g, x, bias, p, ln, L, my_id, my_s))
+      route_token_exact<NP>(row, x, bias, p, ln, my_id, my_s);
   }
   return route_epilogue(my_id, my_s, p, ln, t, ids, wts, packed);
 }
