@@ -74,7 +74,7 @@ __device__ void block_exclusive_scan(const int32_t *in, int n, int32_t *out, int
 // ---------------------------------------------------------------------------
 // Decode path: one launch for T <= 64.
 // ---------------------------------------------------------------------------
-template <int NP>
+template <int NP, int LPG>
 __global__ __launch_bounds__(BLOCK) void route_decode_kernel(
     const float *__restrict__ logits, const float *__restrict__ bias, int T, RouteParams p,
     int32_t *__restrict__ ids, float *__restrict__ wts, int32_t *__restrict__ packed,
@@ -91,9 +91,9 @@ __global__ __launch_bounds__(BLOCK) void route_decode_kernel(
   if (t < T) {
     const float *row = logits + (size_t)t * p.E;
     float b[2 * NP], x[2 * NP];
-    load_lane_layout<NP>(row, p, lane, x);
-    load_lane_layout<NP>(bias, p, lane, b);
-    route_token<NP>(row, x, b, bias, p, lane, t, &scratch[wave], ids, wts, packed);
+    load_lane_layout<NP, LPG>(row, p, lane, x);
+    load_lane_layout<NP, LPG>(bias, p, lane, b);
+    route_token<NP, LPG>(row, x, b, bias, p, lane, t, &scratch[wave], ids, wts, packed);
   }
   // Publish this block's outputs, then take a ticket.
   __threadfence();
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(BLOCK) void route_decode_kernel(
 // ---------------------------------------------------------------------------
 // Prefill path, kernel 1: route tiles of 64 tokens.
 // ---------------------------------------------------------------------------
-template <int NP>
+template <int NP, int LPG>
 __global__ __launch_bounds__(BLOCK) void route_tokens_kernel(
     const float *__restrict__ logits, const float *__restrict__ bias, int T, RouteParams p,
     int32_t *__restrict__ ids, float *__restrict__ wts, int32_t *__restrict__ packed) {
@@ -143,9 +143,9 @@ __global__ __launch_bounds__(BLOCK) void route_tokens_kernel(
   if (t >= T) return;
   const float *row = logits + (size_t)t * p.E;
   float b[2 * NP], x[2 * NP];
-  load_lane_layout<NP>(row, p, lane, x);
-  load_lane_layout<NP>(bias, p, lane, b);
-  route_token<NP>(row, x, b, bias, p, lane, t, &scratch[wave], ids, wts, packed);
+  load_lane_layout<NP, LPG>(row, p, lane, x);
+  load_lane_layout<NP, LPG>(bias, p, lane, b);
+  route_token<NP, LPG>(row, x, b, bias, p, lane, t, &scratch[wave], ids, wts, packed);
 }
 
 // Prefill path, kernel 1b: per tile of TILE_TOKENS tokens, a 64-bit token
@@ -285,13 +285,13 @@ static size_t route_ws_bytes(int T, int e_out, int K) {
   return b;
 }
 
-template <int NP>
+template <int NP, int LPG>
 static hipError_t launch_route(const float *logits, const float *bias, int T, const RouteParams &rp,
                                const moe_route_outputs *o, char *ws, hipStream_t st) {
   if (T <= MOE_ROUTE_MAX_FUSED_TOKENS) {
     const int grid = T > 0 ? (T + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK : 1;
     if (g_ev_before) hipEventRecord(g_ev_before, st);
-    route_decode_kernel<NP><<<grid, BLOCK, 0, st>>>(logits, bias, T, rp, o->topk_ids,
+    route_decode_kernel<NP, LPG><<<grid, BLOCK, 0, st>>>(logits, bias, T, rp, o->topk_ids,
                                                      o->topk_weights, o->packed, o->counts,
                                                      o->offsets, o->perm, o->inv_perm,
                                                      reinterpret_cast<uint32_t *>(ws));
@@ -305,7 +305,7 @@ static hipError_t launch_route(const float *logits, const float *bias, int T, co
   const int cus = cu_count();
   const int nblk = (T + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK;
   if (g_ev_before) hipEventRecord(g_ev_before, st);
-  route_tokens_kernel<NP><<<nblk, BLOCK, 0, st>>>(logits, bias, T, rp, o->topk_ids,
+  route_tokens_kernel<NP, LPG><<<nblk, BLOCK, 0, st>>>(logits, bias, T, rp, o->topk_ids,
                                                    o->topk_weights, o->packed);
   if (g_ev_after) hipEventRecord(g_ev_after, st);
   tile_count_kernel<<<ntiles, BLOCK, 0, st>>>(o->packed, T, rp.K, rp.e_out, hist, ntiles,
@@ -379,15 +379,20 @@ static int route_impl(const float *logits, const float *bias, int32_t T,
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char *ws = reinterpret_cast<char *>(workspace);
   hipError_t err;
+  // the 896-expert, 8-group shape gets constant lanes per group
+  if (rp.E == 896 && rp.lpg == 8) {
+    err = launch_route<7, 8>(logits, bias, T, rp, o, ws, s);
+    return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  }
   switch (rp.E / 128) {
-    case 1: err = launch_route<1>(logits, bias, T, rp, o, ws, s); break;
-    case 2: err = launch_route<2>(logits, bias, T, rp, o, ws, s); break;
-    case 3: err = launch_route<3>(logits, bias, T, rp, o, ws, s); break;
-    case 4: err = launch_route<4>(logits, bias, T, rp, o, ws, s); break;
-    case 5: err = launch_route<5>(logits, bias, T, rp, o, ws, s); break;
-    case 6: err = launch_route<6>(logits, bias, T, rp, o, ws, s); break;
-    case 7: err = launch_route<7>(logits, bias, T, rp, o, ws, s); break;
-    case 8: err = launch_route<8>(logits, bias, T, rp, o, ws, s); break;
+    case 1: err = launch_route<1, 0>(logits, bias, T, rp, o, ws, s); break;
+    case 2: err = launch_route<2, 0>(logits, bias, T, rp, o, ws, s); break;
+    case 3: err = launch_route<3, 0>(logits, bias, T, rp, o, ws, s); break;
+    case 4: err = launch_route<4, 0>(logits, bias, T, rp, o, ws, s); break;
+    case 5: err = launch_route<5, 0>(logits, bias, T, rp, o, ws, s); break;
+    case 6: err = launch_route<6, 0>(logits, bias, T, rp, o, ws, s); break;
+    case 7: err = launch_route<7, 0>(logits, bias, T, rp, o, ws, s); break;
+    case 8: err = launch_route<8, 0>(logits, bias, T, rp, o, ws, s); break;
     default: return MOE_ERR_UNSUPPORTED;
   }
   return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;

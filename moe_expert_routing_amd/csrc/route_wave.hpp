@@ -63,6 +63,18 @@ struct RouteParams {
 // Tokens that took the exact path (diagnostic, moe_route_exact_path_tokens).
 __device__ unsigned long long g_exact_path_tokens = 0ull;
 
+// Lanes per group: a compile-time constant (LPG > 0) or the runtime value
+// (LPG = 0). The common shapes get constant loops and lane indices.
+template <int LPG>
+__device__ __forceinline__ int lpg_of(const RouteParams &p) { return LPG ? LPG : p.lpg; }
+template <int LPG>
+__device__ __forceinline__ int lpg_log2_of(const RouteParams &p) {
+  return LPG ? (LPG == 1 ? 0 : LPG == 2 ? 1 : LPG == 4 ? 2 : LPG == 8 ? 3 : LPG == 16 ? 4 : LPG == 32 ? 5 : 6)
+             : p.lpg_log2;
+}
+template <int LPG>
+__device__ __forceinline__ int groups_of(const RouteParams &p) { return LPG ? 64 / LPG : p.G; }
+
 // Per-wave LDS scratch of the fast path.
 struct WaveScratch {
   uint32_t cand[64];              // candidate expert ids
@@ -78,9 +90,11 @@ constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2,3,0,1]
 constexpr int DPP_HALF_MIRROR = 0x141; // lane i <-> 7-i within 8
 constexpr int DPP_MIRROR = 0x140;      // lane i <-> 15-i within 16
 
+// Every DPP pattern used here reads an in-range lane, so no old value is
+// needed (bound_ctrl set, full masks).
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
 }
 
 template <int CTRL>
@@ -191,15 +205,16 @@ __device__ __forceinline__ float group_err_bound(float v) {
   return 2.02f * FAST_SIG_ERR + 0x1p-17f * v;
 }
 
-template <int NP>
+template <int NP, int LPG>
 __device__ __forceinline__ void load_lane_layout(const float *__restrict__ v, const RouteParams &p,
                                                  int lane, float (&out)[2 * NP]) {
-  const int g = lane >> p.lpg_log2;
-  const int sub = lane & (p.lpg - 1);
-  const float *base = v + g * p.eg + 2 * sub;
+  const int lpg = lpg_of<LPG>(p);
+  const int g = lane >> lpg_log2_of<LPG>(p);
+  const int sub = lane & (lpg - 1);
+  const float *base = v + g * (LPG ? 2 * NP * LPG : p.eg) + 2 * sub;
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
-    const float2 q = *reinterpret_cast<const float2 *>(base + 2 * p.lpg * i);
+    const float2 q = *reinterpret_cast<const float2 *>(base + 2 * lpg * i);
     out[2 * i] = q.x;
     out[2 * i + 1] = q.y;
   }
@@ -240,18 +255,19 @@ __device__ __forceinline__ float score_err(float v) {
 // exact scores (EXACT = true). Returns true, with (id, exact s) of slot
 // k = lane in lanes 0..K-1, only when the result is proven equal to the
 // exact selection.
-template <int NP, bool EXACT>
+template <int NP, int LPG, bool EXACT>
 __device__ __forceinline__ bool select_token(const float *__restrict__ row,
                                              const float *__restrict__ bias_g,
                                              const float (&x)[2 * NP], const float (&bias)[2 * NP],
                                              const RouteParams &p, int lane, WaveScratch *L,
                                              int &my_id, float &my_s) {
   constexpr int M = 2 * NP;
-  const int g = lane >> p.lpg_log2;
-  const int e0 = g * p.eg + 2 * (lane & (p.lpg - 1));
+  const int lpg = lpg_of<LPG>(p), lpg_log2 = lpg_log2_of<LPG>(p), G = groups_of<LPG>(p);
+  const int g = lane >> lpg_log2;
+  const int e0 = g * (LPG ? M * LPG : p.eg) + 2 * (lane & (lpg - 1));
 
   // ---- streaming: scores -> keys -> the lane's top-4 keys ------------------
-  uint32_t p1 = 0u, p2 = 0u, p3 = 0u, p4 = 0u;
+  uint32_t p1 = 0u, p2 = 0u, p3 = 0u, p4 = 0u, p5 = 0u;
   float x1 = -__builtin_inff(), x2 = -__builtin_inff();  // exact top-2 (EXACT)
 #pragma unroll
   for (int q = 0; q < M; ++q) {
@@ -265,6 +281,7 @@ __device__ __forceinline__ bool select_token(const float *__restrict__ row,
       sc = fast_sigmoid(x[q]) + bias[q];
     }
     const uint32_t k = approx_key(sc, q);
+    p5 = umed3(p4, p5, k);
     p4 = umed3(p3, p4, k);
     p3 = umed3(p2, p3, k);
     p2 = umed3(p1, p2, k);
@@ -274,17 +291,17 @@ __device__ __forceinline__ bool select_token(const float *__restrict__ row,
   // ---- groups ---------------------------------------------------------------
   bool kept;
   uint32_t hi_key;  // one above the largest kept key
-  if (!EXACT && p.G <= 8) {
+  if (!EXACT && G <= 8) {
     uint32_t g1 = p1, g2 = p2;
-    group_top2(g1, g2, p.lpg);
+    group_top2(g1, g2, lpg);
     const uint32_t glast = (p.topn == 2) ? g2 : g1;
     const float gs = (p.topn == 2) ? key_value(g1) + key_value(g2) : key_value(g1);  // >= 0
     // every group's score and top key, on the scalar unit
     uint32_t sv[8], top[8];
 #pragma unroll
     for (int gg = 0; gg < 8; ++gg) {
-      const int src = (gg < p.G ? gg : 0) << p.lpg_log2;
-      sv[gg] = gg < p.G ? readlane_u32(__float_as_uint(gs), src) : 0u;
+      const int src = (gg < G ? gg : 0) << lpg_log2;
+      sv[gg] = gg < G ? readlane_u32(__float_as_uint(gs), src) : 0u;
       top[gg] = readlane_u32(g1, src);
     }
     uint32_t srt[8];
@@ -297,14 +314,14 @@ __device__ __forceinline__ bool select_token(const float *__restrict__ row,
       if (i == p.TG - 1) keep_thr = srt[i];
       if (i == p.TG) drop_max = srt[i];
     }
-    if (p.TG < p.G) {
+    if (p.TG < G) {
       const float kmin = __uint_as_float(keep_thr), dmax = __uint_as_float(drop_max);
       if (!(kmin - group_err_bound(kmin) > dmax + group_err_bound(dmax))) return false;
     }
     hi_key = 0u;
 #pragma unroll
     for (int gg = 0; gg < 8; ++gg)
-      if (gg < p.G && sv[gg] >= keep_thr) hi_key = umax(hi_key, top[gg]);
+      if (gg < G && sv[gg] >= keep_thr) hi_key = umax(hi_key, top[gg]);
     hi_key += 1u;
     kept = __float_as_uint(gs) >= keep_thr;
     // the kept groups' scores must rest on unclamped (positive) values
@@ -312,7 +329,7 @@ __device__ __forceinline__ bool select_token(const float *__restrict__ row,
   } else {
     // exact group scores (EXACT), or approximate ones with many groups
     float m1 = EXACT ? x1 : key_value(p1), m2 = EXACT ? x2 : key_value(p2);
-    for (int d = 1; d < p.lpg; d <<= 1) {
+    for (int d = 1; d < lpg; d <<= 1) {
       const float o1 = __shfl_xor(m1, d);
       const float o2 = __shfl_xor(m2, d);
       const float n2 = fmaxf(fminf(m1, o1), fmaxf(m2, o2));
@@ -321,14 +338,14 @@ __device__ __forceinline__ bool select_token(const float *__restrict__ row,
     }
     const float gs = (p.topn == 2) ? (m1 + m2) : m1;
     int rank = 0;
-    for (int gg = 0; gg < p.G; ++gg) {
-      const float o = __uint_as_float(readlane_u32(__float_as_uint(gs), gg << p.lpg_log2));
+    for (int gg = 0; gg < G; ++gg) {
+      const float o = __uint_as_float(readlane_u32(__float_as_uint(gs), gg << lpg_log2));
       rank += ((o > gs) || (EXACT && o == gs && gg < g)) ? 1 : 0;
     }
     kept = rank < p.TG;
     if (!EXACT) {
-      if (p.TG < p.G) {
-        if (__popcll(__ballot(kept)) != (unsigned)(p.TG * p.lpg)) return false;
+      if (p.TG < G) {
+        if (__popcll(__ballot(kept)) != (unsigned)(p.TG * lpg)) return false;
         const uint32_t gsb = __float_as_uint(gs);
         const float kmin = __uint_as_float(wave_min_u32(kept ? gsb : 0x7F7FFFFFu));
         const float dmax = __uint_as_float(wave_max_u32(kept ? 0u : gsb));
@@ -339,23 +356,25 @@ __device__ __forceinline__ bool select_token(const float *__restrict__ row,
     hi_key = wave_max_u32(kept ? p1 : 0u) + 1u;
   }
 
-  // ---- threshold: bisection (value space) on the kept lanes' top-4 --------
+  // ---- threshold: bisection (value space) on the kept lanes' top-5 --------
   const uint32_t q1 = kept ? p1 : 0u, q2 = kept ? p2 : 0u, q3 = kept ? p3 : 0u,
-                 q4 = kept ? p4 : 0u;
+                 q4 = kept ? p4 : 0u, q5 = kept ? p5 : 0u;
   const int need = p.K + 2;
   uint32_t lo = 1u;
   const int c0 = __popcll(__ballot(q1 >= 1u)) + __popcll(__ballot(q2 >= 1u)) +
-                 __popcll(__ballot(q3 >= 1u)) + __popcll(__ballot(q4 >= 1u));
+                 __popcll(__ballot(q3 >= 1u)) + __popcll(__ballot(q4 >= 1u)) +
+                 __popcll(__ballot(q5 >= 1u));
   if (c0 >= need) {
     uint32_t hi = hi_key;
     while (hi - lo > 1u) {
       uint32_t mid = __float_as_uint(0.5f * (key_value(lo) + key_value(hi)));
       if (mid <= lo || mid >= hi) mid = lo + ((hi - lo) >> 1);
       const int c = __popcll(__ballot(q1 >= mid)) + __popcll(__ballot(q2 >= mid)) +
-                    __popcll(__ballot(q3 >= mid)) + __popcll(__ballot(q4 >= mid));
+                    __popcll(__ballot(q3 >= mid)) + __popcll(__ballot(q4 >= mid)) +
+                    __popcll(__ballot(q5 >= mid));
       if (c >= need) {
         lo = mid;
-        if (c <= 32) break;
+        if (c <= 28) break;
       } else {
         hi = mid;
       }
@@ -365,8 +384,8 @@ __device__ __forceinline__ bool select_token(const float *__restrict__ row,
 
   // ---- compaction: candidate expert ids ------------------------------------
   int m = 0;
-  if (__ballot(q4 >= theta) == 0ull) {
-    // no lane has more than 3 keys >= theta: the pool holds them all
+  if (__ballot(q5 >= theta) == 0ull) {
+    // no lane has more than 4 keys >= theta: the pool holds them all
     const uint32_t pool[4] = {q1, q2, q3, q4};
     int base[4];
 #pragma unroll
@@ -379,7 +398,7 @@ __device__ __forceinline__ bool select_token(const float *__restrict__ row,
     for (int i = 0; i < 4; ++i) {
       const bool pr = pool[i] >= theta;
       const uint64_t bm = __ballot(pr);
-      if (pr) L->cand[base[i] + mbcnt(bm)] = (uint32_t)slot_expert(e0, p.lpg, 15 - (int)(pool[i] & 15u));
+      if (pr) L->cand[base[i] + mbcnt(bm)] = (uint32_t)slot_expert(e0, lpg, 15 - (int)(pool[i] & 15u));
     }
   } else {
     // re-scan every slot (keys recomputed)
@@ -397,7 +416,7 @@ __device__ __forceinline__ bool select_token(const float *__restrict__ row,
       const float sc = (EXACT ? sigmoid_rn32(x[q]) : fast_sigmoid(x[q])) + bias[q];
       const bool pr = kept && approx_key(sc, q) >= theta;
       const uint64_t bm = __ballot(pr);
-      if (pr) L->cand[base[q] + mbcnt(bm)] = (uint32_t)slot_expert(e0, p.lpg, q);
+      if (pr) L->cand[base[q] + mbcnt(bm)] = (uint32_t)slot_expert(e0, lpg, q);
     }
   }
   if (m < p.K) return false;
@@ -430,11 +449,13 @@ __device__ __forceinline__ bool select_token(const float *__restrict__ row,
   wave_lds_sync();
 
   // ---- certificate -----------------------------------------------------------
-  // slot k = lane for lanes 0..K-1; lane K holds the best non-winner
+  // slot k = lane for lanes 0..K-1; rank K is the best non-winner
   const bool has_next = m > p.K;
-  uint4 rr = make_uint4(0u, 0u, 0u, 0u);
-  if (lane <= p.K && (lane < p.K || has_next)) rr = L->res[lane];
-  const float rsc = __uint_as_float(rr.w);
+  uint4 rr = make_uint4(0u, 0u, 0u, 0u), nr = make_uint4(0u, 0u, 0u, 0u);
+  if (lane < p.K) {
+    rr = L->res[lane];
+    if (lane < p.K - 1 || has_next) nr = L->res[lane + 1];
+  }
   // the K-th score must beat every non-candidate (keys below theta)
   const float tau = key_value(theta);
   const float kth = __uint_as_float(readlane_u32(rr.w, p.K - 1));
@@ -444,33 +465,38 @@ __device__ __forceinline__ bool select_token(const float *__restrict__ row,
     if (!(kth - score_err(kth) > tau + score_err(tau) + 0x1p-19f * tau)) return false;
     // adjacent winners (and the K-th vs the best non-winner) must be apart
     // by more than the error, or be exact twins (same logit and bias)
-    const uint32_t nsc = __shfl_down(rr.w, 1), nx = __shfl_down(rr.y, 1),
-                   nb = __shfl_down(rr.z, 1);
     const bool check = lane < p.K && (lane < p.K - 1 || has_next);
-    const float nv = __uint_as_float(nsc);
-    const bool sep = (rsc - score_err(rsc)) > (nv + score_err(nv));
-    const bool twin = (rr.y == nx) && (rr.z == nb);
+    const float rv = __uint_as_float(rr.w), nv = __uint_as_float(nr.w);
+    const bool sep = (rv - score_err(rv)) > (nv + score_err(nv));
+    const bool twin = (rr.y == nr.y) && (rr.z == nr.z);
     if (__ballot(check && !(sep || twin))) return false;
   }
-  if (lane < p.K) {
-    my_id = (int)rr.x;
-    my_s = sigmoid_rn32(__uint_as_float(rr.y));  // exact score for the weight
-  }
+  // score for the weight: exact, or (when every winner has logit >= -1.9,
+  // i.e. s >= 1/8) the fast approximation, whose relative error there is
+  // below 2^-21 (checked exhaustively by a GPU test); the weight then stays
+  // within 1e-6 (relative) of the exact one.
+  const float wx = __uint_as_float(rr.y);
+  my_id = (int)rr.x;
+  if (EXACT || __ballot(lane < p.K && !(wx >= -1.9f)))
+    my_s = (lane < p.K) ? sigmoid_rn32(wx) : 0.0f;
+  else
+    my_s = fast_sigmoid(wx);
   return true;
 }
 
 // ---------------------------------------------------------------------------
 // Exact path (every score exact; top-k by wave argmax).
 // ---------------------------------------------------------------------------
-template <int NP>
+template <int NP, int LPG>
 __device__ __forceinline__ void route_token_exact(const float *__restrict__ row,
                                                const float (&x)[2 * NP],
                                                const float (&bias)[2 * NP],
                                                const RouteParams &p, int lane, int &my_id,
                                                float &my_s) {
   constexpr int M = 2 * NP;
-  const int g = lane >> p.lpg_log2;
-  const int e0 = g * p.eg + 2 * (lane & (p.lpg - 1));
+  const int lpg = lpg_of<LPG>(p), lpg_log2 = lpg_log2_of<LPG>(p), G = groups_of<LPG>(p);
+  const int g = lane >> lpg_log2;
+  const int e0 = g * (LPG ? M * LPG : p.eg) + 2 * (lane & (lpg - 1));
 
   float sp[M];
 #pragma unroll
@@ -482,7 +508,7 @@ __device__ __forceinline__ void route_token_exact(const float *__restrict__ row,
     m2 = fmaxf(m2, fminf(m1, sp[q]));
     m1 = fmaxf(m1, sp[q]);
   }
-  for (int d = 1; d < p.lpg; d <<= 1) {
+  for (int d = 1; d < lpg; d <<= 1) {
     const float o1 = __shfl_xor(m1, d);
     const float o2 = __shfl_xor(m2, d);
     const float n2 = fmaxf(fminf(m1, o1), fmaxf(m2, o2));
@@ -491,8 +517,8 @@ __device__ __forceinline__ void route_token_exact(const float *__restrict__ row,
   }
   const float gs = (p.topn == 2) ? (m1 + m2) : m1;
   int rank = 0;
-  for (int gg = 0; gg < p.G; ++gg) {
-    const float o = __shfl(gs, gg << p.lpg_log2);
+  for (int gg = 0; gg < G; ++gg) {
+    const float o = __shfl(gs, gg << lpg_log2);
     rank += (o > gs) || (o == gs && gg < g);
   }
   const bool kept = rank < p.TG;
@@ -505,7 +531,7 @@ __device__ __forceinline__ void route_token_exact(const float *__restrict__ row,
     uint64_t best = 0;
 #pragma unroll
     for (int q = 0; q < M; ++q) {
-      const uint32_t e = (uint32_t)slot_expert(e0, p.lpg, q);
+      const uint32_t e = (uint32_t)slot_expert(e0, lpg, q);
       const uint64_t k = ((uint64_t)ord_f32(sp[q]) << 32) | (uint64_t)(~e);
       best = ((taken >> q) & 1u) ? best : umax64(best, k);
     }
@@ -515,7 +541,7 @@ __device__ __forceinline__ void route_token_exact(const float *__restrict__ row,
     if (lane == r) my_id = (int)win;
 #pragma unroll
     for (int q = 0; q < M; ++q)
-      if ((uint32_t)slot_expert(e0, p.lpg, q) == win) taken |= 1u << q;
+      if ((uint32_t)slot_expert(e0, lpg, q) == win) taken |= 1u << q;
   }
   my_s = (lane < p.K) ? sigmoid_rn32(row[my_id]) : 0.0f;
 }
@@ -548,7 +574,7 @@ __device__ __forceinline__ int route_epilogue(int my_id, float my_s, const Route
 }
 
 // Routes token t whose logits are in x (lane layout; row = the token's row).
-template <int NP>
+template <int NP, int LPG>
 __device__ __forceinline__ int route_token(const float *__restrict__ row,
                                            const float (&x)[2 * NP], const float (&bias)[2 * NP],
                                            const float *__restrict__ bias_g, const RouteParams &p,
@@ -562,10 +588,10 @@ __device__ __forceinline__ int route_token(const float *__restrict__ row,
   asm volatile("" : "+v"(ln));
   int my_id = 0;
   float my_s = 0.0f;
-  if (!select_token<NP, false>(row, bias_g, x, bias, p, ln, L, my_id, my_s)) {
+  if (!select_token<NP, LPG, false>(row, bias_g, x, bias, p, ln, L, my_id, my_s)) {
     if (ln == 0) atomicAdd(&g_exact_path_tokens, 1ull);
-    if (!select_token<NP, true>(row, bias_g, x, bias, p, ln, L, my_id, my_s))
-      route_token_exact<NP>(row, x, bias, p, ln, my_id, my_s);
+    if (!select_token<NP, LPG, true>(row, bias_g, x, bias, p, ln, L, my_id, my_s))
+      route_token_exact<NP, LPG>(row, x, bias, p, ln, my_id, my_s);
   }
   return route_epilogue(my_id, my_s, p, ln, t, ids, wts, packed);
 }
