@@ -33,6 +33,7 @@ METRIC = "routing µs/call at 8/16/64 tokens; routed tokens/s + HBM GB/s at 32K 
 HBM_PEAK_GBPS = 8000.0
 BYTES_PER_TOKEN_PATH = 3904     # logits 3584 + ids, weights, packed, perm, inv (5 x 64)
 BYTES_PER_TOKEN_ROUTE_KERNEL = 3776  # logits 3584 + ids, weights, packed (3 x 64)
+COPY_BYTES = 512 << 20
 PROFILE_PMC = os.path.join(ROOT, "profiles", "pmc_route_tokens_long_prefill_32768.txt")
 
 
@@ -172,6 +173,26 @@ def main():
     log(f"bench: {ms_per_step * 1e3:.1f} us/step, route kernel {kern_avg_ms * 1e3:.1f} us")
 
     # ------------------------------------------------------------------
+    # plain device copy of 512 MiB (HBM reference bandwidth; the same copy
+    # calibrates the FETCH_SIZE / WRITE_SIZE counters)
+    # ------------------------------------------------------------------
+    log("bench: device copy of 512 MiB")
+    csrc_buf = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    cdst_buf = torch.empty_like(csrc_buf)
+    copy_ms = []
+    for rep in range(6):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        cdst_buf.copy_(csrc_buf)
+        b.record()
+        torch.cuda.synchronize()
+        if rep:
+            copy_ms.append(a.elapsed_time(b))
+    copy_gbps = 2 * COPY_BYTES / (statistics.median(copy_ms) * 1e-3) / 1e9
+    del csrc_buf, cdst_buf
+
+    # ------------------------------------------------------------------
     # decode latency
     # ------------------------------------------------------------------
     def time_calls(fn, n, reps=5):
@@ -204,6 +225,11 @@ def main():
         torch.cuda.synchronize()
         return time_calls(g.replay, max(1, n // per_graph), reps) / per_graph
 
+    def empty_launch():
+        torch.cuda._sleep(0)
+
+    floor = {"eager": round(time_calls(empty_launch, args.decode_calls), 2),
+             "hipgraph": round(time_graph(empty_launch, args.decode_calls), 2)}
     decode = {}
     decode_graph = {}
     decode_cases = {8: W.tiny_global(8), 16: W.decode_local(16), 64: W.decode_sweep(64, 0)}
@@ -287,7 +313,9 @@ def main():
                    "top_k": W.K, "local_expert_offset": off, "num_local_experts": cnt,
                    "num_experts_out": e_out, "input_sets_rotated": 3},
         "hbm_gbps_algorithmic_path": round(path_gbps, 1),
+        "copy_gbps_512MiB": round(copy_gbps, 1),
         "decode_us_per_call": decode,
+        "empty_kernel_us_per_call": floor,
         "decode_us_per_call_hipgraph": decode_graph,
         "router_gemm_route": gemm,
         "roofline": {"bound": "hbm", "kernel": "route_tokens_kernel",
@@ -295,6 +323,7 @@ def main():
                      "frac": round(frac, 4),
                      "kernel_us_avg": round(kern_avg_ms * 1e3, 2),
                      "bytes_per_token": BYTES_PER_TOKEN_ROUTE_KERNEL,
+                     "frac_of_copy": round(kern_gbps / copy_gbps, 4),
                      "traffic": (round(traffic, 0) if traffic is not None else None),
                      "source_digest": digest},
         "cpu_baseline": cpu,
