@@ -172,6 +172,15 @@ def main():
     traffic = read_traffic(digest)
     log(f"bench: {ms_per_step * 1e3:.1f} us/step, route kernel {kern_avg_ms * 1e3:.1f} us")
 
+    # which kernel path the tokens of one step took
+    for path in (M.PATH_EXACT, M.PATH_REFINED, M.PATH_REROUTED):
+        M.path_tokens(path, reset=True)
+    step(0)
+    torch.cuda.synchronize()
+    paths = {"tokens": T, "exact_refinement": M.path_tokens(M.PATH_REFINED, reset=True),
+             "rerouted_one_token_per_wave": M.path_tokens(M.PATH_REROUTED, reset=True),
+             "exact_pipeline": M.path_tokens(M.PATH_EXACT, reset=True)}
+
     # ------------------------------------------------------------------
     # plain device copy of 512 MiB (HBM reference bandwidth; the same copy
     # calibrates the FETCH_SIZE / WRITE_SIZE counters)
@@ -313,6 +322,7 @@ def main():
                    "top_k": W.K, "local_expert_offset": off, "num_local_experts": cnt,
                    "num_experts_out": e_out, "input_sets_rotated": 3},
         "hbm_gbps_algorithmic_path": round(path_gbps, 1),
+        "token_paths_per_step": paths,
         "copy_gbps_512MiB": round(copy_gbps, 1),
         "decode_us_per_call": decode,
         "empty_kernel_us_per_call": floor,

@@ -188,6 +188,21 @@ int moe_route_set_kernel_events(void *before, void *after);
  */
 int64_t moe_route_exact_path_tokens(int32_t reset);
 
+/*
+ * Diagnostic: tokens per kernel path since the last reset, summed over calls
+ * on the current device. Synchronises with the device.
+ *   path 0: the one-token-per-wave exact pipeline (as
+ *           moe_route_exact_path_tokens);
+ *   path 1: the exact refinement of the four-tokens-per-wave prefill path
+ *           (896 experts, 8 groups, top_k <= 16, more than 64 tokens), taken
+ *           when its fast certificate does not hold;
+ *   path 2: tokens of that path routed again one token per wave because the
+ *           refinement could not decide either.
+ * reset != 0 zeroes that path's count. Returns the count, MOE_ERR_UNSUPPORTED
+ * for another path, or MOE_ERR_HIP.
+ */
+int64_t moe_route_path_tokens(int32_t path, int32_t reset);
+
 /* Human-readable name of a moe_status value. */
 const char *moe_route_status_string(int status);
 

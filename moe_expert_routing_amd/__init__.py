@@ -60,6 +60,7 @@ EXPORTS = {
     "moe_sigmoid_rn32": (ctypes.c_int, [_c_vp, _c_vp, ctypes.c_int64, _c_i32, _c_vp]),
     "moe_route_set_kernel_events": (ctypes.c_int, [_c_vp, _c_vp]),
     "moe_route_exact_path_tokens": (ctypes.c_int64, [_c_i32]),
+    "moe_route_path_tokens": (ctypes.c_int64, [_c_i32, _c_i32]),
 }
 
 _LIB = None
@@ -254,6 +255,18 @@ def exact_path_tokens(reset: bool = False) -> int:
     v = lib().moe_route_exact_path_tokens(1 if reset else 0)
     if v < 0:
         _check(int(v), "moe_route_exact_path_tokens")
+    return int(v)
+
+
+PATH_EXACT, PATH_REFINED, PATH_REROUTED = 0, 1, 2
+
+
+def path_tokens(path: int, reset: bool = False) -> int:
+    """Diagnostic: tokens that took a kernel path since the last reset
+    (PATH_EXACT, PATH_REFINED or PATH_REROUTED; see moe_route_path_tokens)."""
+    v = lib().moe_route_path_tokens(path, 1 if reset else 0)
+    if v < 0:
+        _check(int(v), "moe_route_path_tokens")
     return int(v)
 
 

@@ -25,6 +25,7 @@
 
 #include "../../include/moe_route.h"
 #include "internal.hpp"
+#include "route_rows.hpp"
 #include "route_wave.hpp"
 
 static_assert(moe::kMaxTopK == MOE_ROUTE_MAX_TOPK, "top-k capacity");
@@ -146,6 +147,45 @@ __global__ __launch_bounds__(BLOCK) void route_tokens_kernel(
   load_lane_layout<NP, LPG>(row, p, lane, x);
   load_lane_layout<NP, LPG>(bias, p, lane, b);
   route_token<NP, LPG>(row, x, b, bias, p, lane, t, &scratch[wave], ids, wts, packed);
+}
+
+// Prefill path, kernel 1 for the 896-expert, 8-group shape: four tokens per
+// wave (route_rows.hpp); rows that fail their certificate are routed again
+// one token per wave.
+__device__ unsigned long long g_row_fallback_tokens = 0ull;
+
+__global__ __launch_bounds__(BLOCK, 8) void route_rows_kernel(
+    const float *__restrict__ logits, const float *__restrict__ bias, int T, RouteParams p,
+    int32_t *__restrict__ ids, float *__restrict__ wts, int32_t *__restrict__ packed) {
+  __shared__ float bias_lds[rows::G * rows::BIAS_GSTRIDE];
+  __shared__ union {
+    rows::RowScratch r;
+    WaveScratch w;
+  } scratch[WAVES_PER_BLOCK];
+  __shared__ int bad_bias;
+  const bool ok = rows::stage_bias<BLOCK>(bias, bias_lds, &bad_bias);  // all threads, before any exit
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int64_t t0 = ((int64_t)blockIdx.x * WAVES_PER_BLOCK + wave) * 4;
+  if (t0 >= T) return;
+  uint32_t redo = 0xFu;
+  if (ok)
+    redo = rows::route_rows4(logits, bias, bias_lds, T, t0, p, lane, &scratch[wave].r, ids, wts,
+                             packed);
+  redo = (uint32_t)__builtin_amdgcn_readfirstlane((int)redo);
+  while (redo) {
+    const int r = __builtin_ctz(redo);
+    redo &= redo - 1u;
+    const int64_t t = t0 + r;
+    if (t >= T) break;
+    if (lane == 0) atomicAdd(&g_row_fallback_tokens, 1ull);
+    const float *row = logits + (size_t)t * p.E;
+    float b[14], x[14];
+    load_lane_layout<7, 8>(row, p, lane, x);
+    load_lane_layout<7, 8>(bias, p, lane, b);
+    route_token<7, 8>(row, x, b, bias, p, lane, t, &scratch[wave].w, ids, wts, packed,
+                      /*fast_first=*/false);
+  }
 }
 
 // Prefill path, kernel 1b: per tile of TILE_TOKENS tokens, a 64-bit token
@@ -285,6 +325,14 @@ static size_t route_ws_bytes(int T, int e_out, int K) {
   return b;
 }
 
+// The four-tokens-per-wave path: 896 experts in 8 groups, top_k <= 16, and
+// kept lanes whose pools (6 usable keys each) can hold top_k + 1 entries;
+// float4 loads need 16-byte aligned rows.
+static bool rows_path_applies(const RouteParams &rp, const float *logits) {
+  return rp.E == rows::E && rp.G == rows::G && rp.K <= rows::MAX_K &&
+         12 * rp.TG >= rp.K + 1 && ((uintptr_t)logits % 16) == 0;
+}
+
 template <int NP, int LPG>
 static hipError_t launch_route(const float *logits, const float *bias, int T, const RouteParams &rp,
                                const moe_route_outputs *o, char *ws, hipStream_t st) {
@@ -303,10 +351,16 @@ static hipError_t launch_route(const float *logits, const float *bias, int T, co
   int32_t *tile_rank = reinterpret_cast<int32_t *>(
       ws + CONTROL_BYTES + align256((size_t)rp.e_out * ntiles * sizeof(int32_t)));
   const int cus = cu_count();
-  const int nblk = (T + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK;
   if (g_ev_before) hipEventRecord(g_ev_before, st);
-  route_tokens_kernel<NP, LPG><<<nblk, BLOCK, 0, st>>>(logits, bias, T, rp, o->topk_ids,
-                                                   o->topk_weights, o->packed);
+  if (LPG == 8 && NP == 7 && rows_path_applies(rp, logits)) {
+    const int nblk = (T + 4 * WAVES_PER_BLOCK - 1) / (4 * WAVES_PER_BLOCK);
+    route_rows_kernel<<<nblk, BLOCK, 0, st>>>(logits, bias, T, rp, o->topk_ids, o->topk_weights,
+                                              o->packed);
+  } else {
+    const int nblk = (T + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK;
+    route_tokens_kernel<NP, LPG><<<nblk, BLOCK, 0, st>>>(logits, bias, T, rp, o->topk_ids,
+                                                     o->topk_weights, o->packed);
+  }
   if (g_ev_after) hipEventRecord(g_ev_after, st);
   tile_count_kernel<<<ntiles, BLOCK, 0, st>>>(o->packed, T, rp.K, rp.e_out, hist, ntiles,
                                               tile_rank);
@@ -455,6 +509,23 @@ int64_t moe_route_exact_path_tokens(int32_t reset) {
     const unsigned long long z = 0;
     if (hipMemcpyToSymbol(HIP_SYMBOL(moe::g_exact_path_tokens), &z, sizeof(z)) != hipSuccess)
       return MOE_ERR_HIP;
+  }
+  return (int64_t)v;
+}
+
+int64_t moe_route_path_tokens(int32_t path, int32_t reset) {
+  unsigned long long *sym = nullptr;
+  switch (path) {
+    case 0: return moe_route_exact_path_tokens(reset);
+    case 1: sym = &moe::rows::g_refined_tokens; break;
+    case 2: sym = &moe::g_row_fallback_tokens; break;
+    default: return MOE_ERR_UNSUPPORTED;
+  }
+  unsigned long long v = 0ull;
+  if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(*sym), sizeof(v)) != hipSuccess) return MOE_ERR_HIP;
+  if (reset) {
+    const unsigned long long z = 0ull;
+    if (hipMemcpyToSymbol(HIP_SYMBOL(*sym), &z, sizeof(z)) != hipSuccess) return MOE_ERR_HIP;
   }
   return (int64_t)v;
 }

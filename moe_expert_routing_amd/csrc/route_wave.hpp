@@ -471,16 +471,10 @@ __device__ __forceinline__ bool select_token(const float *__restrict__ row,
     const bool twin = (rr.y == nr.y) && (rr.z == nr.z);
     if (__ballot(check && !(sep || twin))) return false;
   }
-  // score for the weight: exact, or (when every winner has logit >= -1.9,
-  // i.e. s >= 1/8) the fast approximation, whose relative error there is
-  // below 2^-21 (checked exhaustively by a GPU test); the weight then stays
-  // within 1e-6 (relative) of the exact one.
+  // the weights use the exact s of the winners
   const float wx = __uint_as_float(rr.y);
   my_id = (int)rr.x;
-  if (EXACT || __ballot(lane < p.K && !(wx >= -1.9f)))
-    my_s = (lane < p.K) ? sigmoid_rn32(wx) : 0.0f;
-  else
-    my_s = fast_sigmoid(wx);
+  my_s = (lane < p.K) ? sigmoid_rn32(wx) : 0.0f;
   return true;
 }
 
@@ -580,7 +574,8 @@ __device__ __forceinline__ int route_token(const float *__restrict__ row,
                                            const float *__restrict__ bias_g, const RouteParams &p,
                                            int lane, int64_t t, WaveScratch *L,
                                            int32_t *__restrict__ ids, float *__restrict__ wts,
-                                           int32_t *__restrict__ packed) {
+                                           int32_t *__restrict__ packed,
+                                           bool fast_first = true) {
   // Lane-derived values (expert ids of the slots, ...) are cheap to
   // recompute; an opaque copy of the lane index keeps the compiler from
   // hoisting them out of the caller's token loop into dozens of registers.
@@ -588,7 +583,7 @@ __device__ __forceinline__ int route_token(const float *__restrict__ row,
   asm volatile("" : "+v"(ln));
   int my_id = 0;
   float my_s = 0.0f;
-  if (!select_token<NP, LPG, false>(row, bias_g, x, bias, p, ln, L, my_id, my_s)) {
+  if (!fast_first || !select_token<NP, LPG, false>(row, bias_g, x, bias, p, ln, L, my_id, my_s)) {
     if (ln == 0) atomicAdd(&g_exact_path_tokens, 1ull);
     if (!select_token<NP, LPG, true>(row, bias_g, x, bias, p, ln, L, my_id, my_s))
       route_token_exact<NP, LPG>(row, x, bias, p, ln, my_id, my_s);
