@@ -157,7 +157,7 @@ __device__ unsigned long long g_row_fallback_tokens = 0ull;
 __global__ __launch_bounds__(BLOCK, 8) void route_rows_kernel(
     const float *__restrict__ logits, const float *__restrict__ bias, int T, RouteParams p,
     int32_t *__restrict__ ids, float *__restrict__ wts, int32_t *__restrict__ packed) {
-  __shared__ float bias_lds[rows::G * rows::BIAS_GSTRIDE];
+  __shared__ float bias_lds[rows::E];
   __shared__ union {
     rows::RowScratch r;
     WaveScratch w;

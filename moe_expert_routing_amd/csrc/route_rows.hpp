@@ -8,34 +8,41 @@
 // "[kimi-k3] Rank-local expert ids for the EP routed MoE (upstream #45544)",
 // commit message). Routing four tokens with one instruction stream shares
 // every cross-lane step between them, and all cross-lane traffic stays inside
-// a DPP row, so the selection needs no scalar-unit work per token.
+// a DPP row, so the selection needs almost no scalar-unit work.
 //
-// Lane layout. Lane l: row r = l / 16 (token t0 + r), u = l % 16, group
-// g = u / 2, sub = u % 2. The lane holds the 56 experts
-//   e(q) = 112 g + 4 sub + 8 (q / 4) + (q % 4),   slot q < 56,
-// read as 14 float4 loads; within a lane, expert ids increase with the slot.
+// Lane layout. Lane l: row r = l / 16 (token t0 + r), u = l % 16, quad
+// c = u / 4, sub = u % 4. In pass 0 the lane reads group c, in pass 1 group
+// c + 4; its slot q = 28 pass + 4 i + j (i < 7, j < 4) is expert
+//   e(q) = 112 (c + 4 pass) + 4 sub + 16 i + j,
+// so the four lanes of a group read 64 contiguous bytes per load, and expert
+// ids increase with the slot.
 //
 // Keys. v = fl32(s~ + fl32(b + 3)) with s~ the hardware exp2/rcp sigmoid.
 // Whenever b >= -1, v lies in [2, 512), a range in which the top 6 bits of
 // the binary32 pattern are constant, so
 //   key = (bits(v) << 6) | (63 - q)
-// orders by v at full binary32 resolution, then by lower slot. |v - (sp +
-// 3)| <= row_err(v) (sp the exact biased score); see row_err.
+// orders by v at full binary32 resolution, then by lower slot (lower id).
+// |v - (sp + 3)| <= row_err(v) (sp the exact biased score); see row_err.
 //
 // Selection.
-//  1. Each lane keeps its top-10 keys (v_max_u32 + nine v_med3_u32 per key).
-//  2. Group score from the lane pair's top-2; group ranks by comparing
-//     unique integer group keys around the row (row_ror); the choice is
-//     certified by the margin between the kept and the dropped groups.
-//  3. top_k + 1 rounds of row-maximum extraction over the kept lanes' pool
-//     heads: the first top_k are the winners, the last bounds every other
-//     expert of the kept groups from above.
+//  1. Each lane keeps its top-8 keys of each pass (v_max_u32 + seven
+//     v_med3_u32 per key).
+//  2. Group scores from the quad's top-2 of each pass; group ranks by
+//     comparing unique integer group keys around the row (row_ror); the
+//     choice is certified by the margin between the kept and the dropped
+//     groups.
+//  3. The kept pools of a lane are merged (bitonic) into one sorted top-10;
+//     top_k + 1 rounds of row-maximum extraction over the heads give the
+//     winners, and the last bounds every other expert of the kept groups.
 //  4. The winners are scored exactly (RN32 sigmoid, fl32 bias add) and
 //     ranked by (sp desc, id asc); the result is accepted when the weakest
 //     winner's exact score beats that bound, exactly top_k + 1 keys were
-//     taken (no equal keys) and no lane used up its pool.
-// A row that fails a check is routed again by the one-token-per-wave exact
-// pipeline of route_wave.hpp.
+//     taken (no equal keys) and no pool was used up.
+// A row that fails a check is settled by an exact refinement in the same
+// layout (exact group scores, exact scores of every candidate in the error
+// band); only a row the refinement cannot decide either (ties denser than
+// the pools) is routed again by the one-token-per-wave exact pipeline of
+// route_wave.hpp.
 #pragma once
 
 #include "route_wave.hpp"
@@ -49,18 +56,16 @@ __device__ unsigned long long g_refined_tokens = 0ull;
 constexpr int E = 896;
 constexpr int G = 8;
 constexpr int EG = 112;
-constexpr int LANES = 16;     // lanes per token (one DPP row)
-constexpr int NQ = 14;        // float4 loads per lane
-constexpr int SLOTS = 4 * NQ; // experts per lane
-constexpr int POOL = 10;      // keys kept per lane
-constexpr int MAX_K = 16;     // top_k handled by this path
-constexpr int BIAS_GSTRIDE = 120;  // LDS floats per group: b128 reads hit 64 distinct banks
-constexpr float BIAS_SHIFT = 3.0f;
-
-constexpr int DPP_ROR2 = 0x122, DPP_ROR4 = 0x124, DPP_ROR6 = 0x126, DPP_ROR8 = 0x128,
-              DPP_ROR10 = 0x12A, DPP_ROR12 = 0x12C, DPP_ROR14 = 0x12E;
-
+constexpr int LANES = 16;   // lanes per token (one DPP row)
+constexpr int NQP = 7;      // float4 loads per lane and pass
+constexpr int PP = 8;       // keys kept per lane and pass
+constexpr int POOL = 10;    // merged keys of the kept groups per lane
+constexpr int MAX_K = 16;   // top_k handled by this path
 constexpr int MAX_CAND = 32;  // exact candidates per row in the refinement
+constexpr float BIAS_SHIFT = 3.0f;
+constexpr int PREFETCH = 3;   // float4 loads in flight per lane
+
+constexpr int DPP_ROR4 = 0x124, DPP_ROR8 = 0x128, DPP_ROR12 = 0x12C;
 
 // Per-wave LDS of the row path, by row: winner / candidate ids, exact keys
 // and scores, the final (id, s) by slot.
@@ -69,7 +74,6 @@ struct RowScratch {
   int32_t cnt[4][LANES];
   int32_t cand[4][MAX_CAND];
   unsigned long long ekey[4][MAX_CAND];
-  float sval[4][MAX_CAND];
   uint2 slot[4][MAX_K];
   float kth[4];
 };
@@ -86,44 +90,18 @@ __device__ __forceinline__ float row_group_err(float v) {
 
 __device__ __forceinline__ float key_v(uint32_t k) { return __uint_as_float((k >> 6) | 0x40000000u); }
 
-// Expert id of a key held by the lane whose first expert is `base`.
-__device__ __forceinline__ int key_expert(uint32_t k, int base) {
+// Expert id of a key held by the lane (quad c, sub).
+__device__ __forceinline__ int key_expert(uint32_t k, int c, int sub) {
   const int q = 63 - (int)(k & 63u);
-  return base + q + (q & ~3);
+  const int pass = q >= 28 ? 1 : 0;
+  const int qq = q - 28 * pass;
+  return (c + 4 * pass) * EG + 4 * sub + 16 * (qq >> 2) + (qq & 3);
 }
+__device__ __forceinline__ bool key_pass1(uint32_t k) { return (int)(k & 63u) <= 63 - 28; }
 
 // Inverse of ord_f32.
 __device__ __forceinline__ float ord_inv(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
-}
-
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
-  return ((uint64_t)dpp<CTRL>((uint32_t)(v >> 32)) << 32) | dpp<CTRL>((uint32_t)v);
-}
-
-// Number of the other 7 groups of the row whose key is larger (keys unique).
-template <typename KT>
-__device__ __forceinline__ int group_rank(KT gk) {
-  int n = 0;
-  if constexpr (sizeof(KT) == 8) {
-    n += dpp_u64<DPP_ROR2>(gk) > gk ? 1 : 0;
-    n += dpp_u64<DPP_ROR4>(gk) > gk ? 1 : 0;
-    n += dpp_u64<DPP_ROR6>(gk) > gk ? 1 : 0;
-    n += dpp_u64<DPP_ROR8>(gk) > gk ? 1 : 0;
-    n += dpp_u64<DPP_ROR10>(gk) > gk ? 1 : 0;
-    n += dpp_u64<DPP_ROR12>(gk) > gk ? 1 : 0;
-    n += dpp_u64<DPP_ROR14>(gk) > gk ? 1 : 0;
-  } else {
-    n += dpp<DPP_ROR2>(gk) > gk ? 1 : 0;
-    n += dpp<DPP_ROR4>(gk) > gk ? 1 : 0;
-    n += dpp<DPP_ROR6>(gk) > gk ? 1 : 0;
-    n += dpp<DPP_ROR8>(gk) > gk ? 1 : 0;
-    n += dpp<DPP_ROR10>(gk) > gk ? 1 : 0;
-    n += dpp<DPP_ROR12>(gk) > gk ? 1 : 0;
-    n += dpp<DPP_ROR14>(gk) > gk ? 1 : 0;
-  }
-  return n;
 }
 
 __device__ __forceinline__ uint32_t row_max(uint32_t v) {
@@ -151,9 +129,35 @@ __device__ __forceinline__ double row_sum_f64(double v) {
   return v + dpp_f64<DPP_MIRROR>(v);
 }
 
-// Stages fl32(b + 3) in the row layout (block of `threads` threads); returns
-// false (block-uniform) when some bias lies outside [-1, 500), where the key
-// encoding does not hold. `bad` is an LDS word.
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  return ((uint64_t)dpp<CTRL>((uint32_t)(v >> 32)) << 32) | dpp<CTRL>((uint32_t)v);
+}
+
+// Ranks of the lane's two groups (keys a: group c, b: group c + 4) among
+// the row's 8 groups: the number of larger keys (keys are unique).
+template <typename KT>
+__device__ __forceinline__ void group_ranks(KT a, KT b, int &ra, int &rb) {
+  KT o[6];
+  if constexpr (sizeof(KT) == 8) {
+    o[0] = dpp_u64<DPP_ROR4>(a); o[1] = dpp_u64<DPP_ROR8>(a); o[2] = dpp_u64<DPP_ROR12>(a);
+    o[3] = dpp_u64<DPP_ROR4>(b); o[4] = dpp_u64<DPP_ROR8>(b); o[5] = dpp_u64<DPP_ROR12>(b);
+  } else {
+    o[0] = dpp<DPP_ROR4>(a); o[1] = dpp<DPP_ROR8>(a); o[2] = dpp<DPP_ROR12>(a);
+    o[3] = dpp<DPP_ROR4>(b); o[4] = dpp<DPP_ROR8>(b); o[5] = dpp<DPP_ROR12>(b);
+  }
+  ra = b > a ? 1 : 0;
+  rb = a > b ? 1 : 0;
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    ra += o[i] > a ? 1 : 0;
+    rb += o[i] > b ? 1 : 0;
+  }
+}
+
+// Stages fl32(b + 3) (in expert order) for a block of THREADS threads;
+// returns false (block-uniform) when some bias lies outside [-1, 500),
+// where the key encoding does not hold. `bad` is an LDS word.
 template <int THREADS>
 __device__ __forceinline__ bool stage_bias(const float *__restrict__ bias, float *lds, int *bad) {
   if (threadIdx.x == 0) *bad = 0;
@@ -165,12 +169,126 @@ __device__ __forceinline__ bool stage_bias(const float *__restrict__ bias, float
     if (e < E) {
       const float bb = bias[e] + BIAS_SHIFT;
       ok = ok && (bb >= 2.0f) && (bb < 503.0f);
-      lds[(e / EG) * BIAS_GSTRIDE + (e % EG)] = bb;
+      lds[e] = bb;
     }
   }
   if (!ok) *bad = 1;
   __syncthreads();
   return *bad == 0;
+}
+
+// Streams the lane's 56 experts of the token at `row`: keys into the sorted
+// top-8 of each pass (a: pass 0, b: pass 1).
+__device__ __forceinline__ void stream_pools(const float *__restrict__ row,
+                                             const float *__restrict__ bias_lds, int c, int sub,
+                                             uint32_t (&a)[PP], uint32_t (&b)[PP]) {
+  const float4 *xp = reinterpret_cast<const float4 *>(row + c * EG + 4 * sub);
+  const float4 *bp = reinterpret_cast<const float4 *>(bias_lds + c * EG + 4 * sub);
+  // float4 n (n < 14) of the lane: pass n / 7, load n % 7
+  auto off = [](int n) { return (n / NQP) * EG + 4 * (n % NQP); };
+#pragma unroll
+  for (int i = 0; i < PP; ++i) a[i] = b[i] = 0u;
+  float4 xq[PREFETCH];
+#pragma unroll
+  for (int n = 0; n < PREFETCH; ++n) xq[n] = xp[off(n)];
+#pragma unroll
+  for (int n = 0; n < 2 * NQP; ++n) {
+    const float4 xv = xq[n % PREFETCH];
+    if (n + PREFETCH < 2 * NQP) xq[n % PREFETCH] = xp[off(n + PREFETCH)];
+    const float4 bv = bp[off(n)];
+    const float xs[4] = {xv.x, xv.y, xv.z, xv.w};
+    const float bs[4] = {bv.x, bv.y, bv.z, bv.w};
+    uint32_t(&pl)[PP] = n < NQP ? a : b;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float v = fast_sigmoid(xs[j]) + bs[j];
+      const uint32_t k = (__float_as_uint(v) << 6) | (uint32_t)(63 - (4 * n + j));
+#pragma unroll
+      for (int i = PP - 1; i > 0; --i) pl[i] = umed3(pl[i - 1], pl[i], k);
+      pl[0] = umax(pl[0], k);
+    }
+    // materialise the pool here: otherwise the compiler sinks the lower
+    // pool levels to the end and keeps every intermediate key alive
+    asm volatile("" : "+v"(pl[0]), "+v"(pl[1]), "+v"(pl[2]), "+v"(pl[3]), "+v"(pl[4]),
+                 "+v"(pl[5]), "+v"(pl[6]), "+v"(pl[7]));
+  }
+}
+
+// Approximate group stage: the quad's top-2 of each pass, group scores,
+// kept flags, and whether the choice is certified.
+__device__ __forceinline__ bool approx_groups(const uint32_t (&a)[PP], const uint32_t (&b)[PP],
+                                              const RouteParams &p, int c, bool &kept_a,
+                                              bool &kept_b) {
+  uint32_t a1 = a[0], a2 = a[1], b1 = b[0], b2 = b[1];
+  top2_merge(a1, a2, dpp<DPP_XOR1>(a1), dpp<DPP_XOR1>(a2));
+  top2_merge(a1, a2, dpp<DPP_XOR2>(a1), dpp<DPP_XOR2>(a2));
+  top2_merge(b1, b2, dpp<DPP_XOR1>(b1), dpp<DPP_XOR1>(b2));
+  top2_merge(b1, b2, dpp<DPP_XOR2>(b1), dpp<DPP_XOR2>(b2));
+  const float ga = (p.topn == 2) ? key_v(a1) + key_v(a2) : key_v(a1);  // in [2, 1030)
+  const float gb = (p.topn == 2) ? key_v(b1) + key_v(b2) : key_v(b1);
+  // unique group keys: score bits (the top 3 bits are constant), then lower group
+  const uint32_t ka = (__float_as_uint(ga) << 3) | (uint32_t)(7 - c);
+  const uint32_t kb = (__float_as_uint(gb) << 3) | (uint32_t)(3 - c);
+  int ra, rb;
+  group_ranks(ka, kb, ra, rb);
+  kept_a = ra < p.TG;
+  kept_b = rb < p.TG;
+  // certified when the weakest kept group beats the strongest dropped one
+  // by more than both error bounds
+  const uint32_t ba = __float_as_uint(ga), bb = __float_as_uint(gb);
+  const float kmin = __uint_as_float(
+      row_min(umin(kept_a ? ba : 0x7F7FFFFFu, kept_b ? bb : 0x7F7FFFFFu)));
+  const float dmax = __uint_as_float(row_max(umax(kept_a ? 0u : ba, kept_b ? 0u : bb)));
+  return kmin - row_group_err(kmin) > dmax + row_group_err(dmax);
+}
+
+// Descending compare-exchange.
+__device__ __forceinline__ void cx(uint32_t &x, uint32_t &y) {
+  const uint32_t h = umax(x, y), l = umin(x, y);
+  x = h;
+  y = l;
+}
+
+// Sorted top-POOL of the kept pools: a bitonic merge of a (descending) with
+// b (descending), keeping the first ten.
+__device__ __forceinline__ void merge_kept(const uint32_t (&a)[PP], const uint32_t (&b)[PP],
+                                           bool kept_a, bool kept_b, uint32_t (&m)[POOL]) {
+  uint32_t h[PP], l[PP];
+#pragma unroll
+  for (int i = 0; i < PP; ++i) {
+    const uint32_t x = kept_a ? a[i] : 0u, y = kept_b ? b[PP - 1 - i] : 0u;
+    h[i] = umax(x, y);  // the top 8 of the union, a bitonic sequence
+    l[i] = umin(x, y);  // the rest, bitonic, all below h
+  }
+  cx(h[0], h[4]); cx(h[1], h[5]); cx(h[2], h[6]); cx(h[3], h[7]);
+  cx(h[0], h[2]); cx(h[1], h[3]); cx(h[4], h[6]); cx(h[5], h[7]);
+  cx(h[0], h[1]); cx(h[2], h[3]); cx(h[4], h[5]); cx(h[6], h[7]);
+  cx(l[0], l[4]); cx(l[1], l[5]); cx(l[2], l[6]); cx(l[3], l[7]);
+  cx(l[0], l[2]); cx(l[1], l[3]);
+  cx(l[0], l[1]);
+#pragma unroll
+  for (int i = 0; i < PP; ++i) m[i] = h[i];
+  m[8] = l[0];
+  m[9] = l[1];
+}
+
+// top_k + 1 rounds of row maximum over the heads of m (sorted, descending).
+// rounds: bit (K - round) set when this lane won that round; returns the
+// last maximum (the (top_k+1)-th key).
+__device__ __forceinline__ uint32_t extract(const uint32_t (&m)[POOL], int K, uint32_t &rounds) {
+  uint32_t q[POOL];
+#pragma unroll
+  for (int i = 0; i < POOL; ++i) q[i] = m[i];
+  uint32_t M = 0u;
+  rounds = 0u;
+  for (int rd = 0; rd <= K; ++rd) {
+    M = row_max(q[0]);
+    const bool win = q[0] == M;
+    rounds = rounds + rounds + (win ? 1u : 0u);
+#pragma unroll
+    for (int i = 0; i < POOL - 1; ++i) q[i] = win ? q[i + 1] : q[i];
+  }
+  return M;
 }
 
 // Row epilogue: lane u of a row whose `out` is set holds slot u's (id, s)
@@ -195,83 +313,101 @@ __device__ __forceinline__ void row_outputs(bool out, uint2 sl, const RouteParam
 }
 
 // Number of pool entries (sorted by key) whose value is >= thr.
-__device__ __forceinline__ int pool_count_ge(const uint32_t (&pool)[POOL], double thr) {
-  int c = 0;
+__device__ __forceinline__ int pool_count_ge(const uint32_t (&pl)[PP], double thr) {
+  int n = 0;
 #pragma unroll
-  for (int i = 0; i < POOL; ++i) c += ((double)key_v(pool[i]) >= thr) ? 1 : 0;
-  return c;
+  for (int i = 0; i < PP; ++i) n += ((double)key_v(pl[i]) >= thr) ? 1 : 0;
+  return n;
 }
 
-// Exact refinement of the rows with `need` set (call with the whole wave).
-// Exact group scores from every pool entry that can hold a group's top
-// scores, then the exact top_k from every kept-pool entry within twice the
-// key error of the (top_k+1)-th extracted key; both steps decide from exact
-// scores, so they can only fail when a lane's pool is too short or the
-// candidates exceed MAX_CAND. Returns true (row-uniform) when the row has
-// been written.
-__device__ __forceinline__ bool refine_rows(const float *__restrict__ row,
-                                         const float *__restrict__ bias_g,
-                                         const uint32_t (&pool)[POOL], uint32_t m1, uint32_t m2,
-                                         bool need, const RouteParams &p, int r, int u, int g,
-                                         int base, int64_t t, RowScratch *L,
-                                         int32_t *__restrict__ ids, float *__restrict__ wts,
-                                         int32_t *__restrict__ packed) {
-  const int K = p.K;
-  bool fail = false;
-  if (need && u == 0) atomicAdd(&g_refined_tokens, 1ull);
-
-  // ---- exact group scores ------------------------------------------------------
-  // An expert whose key value is below thr1 is beaten, even exactly, by the
-  // two experts holding the group's approximate top-2 keys.
-  const float v1 = key_v(m1);
-  const double thr1 = (double)(p.topn == 2 ? key_v(m2) : v1) - 2.0 * (double)row_err(v1);
-  const int c1 = need ? pool_count_ge(pool, thr1) : 0;
-  fail = fail || row_max(c1 >= POOL ? 1u : 0u) != 0u;
-  uint32_t t1 = 0u, t2 = 0u;  // exact top-2 of the lane's candidates (ord keys)
+// Exact top-2 (ord keys, with multiplicity) of the first n entries of pl,
+// merged over the quad (the group's four lanes).
+__device__ __forceinline__ void exact_top2(const float *__restrict__ row,
+                                           const float *__restrict__ bias_g,
+                                           const uint32_t (&pl)[PP], int n, int c, int sub,
+                                           uint32_t &t1, uint32_t &t2) {
+  t1 = t2 = 0u;
 #pragma unroll
-  for (int i = 0; i < POOL; ++i) {
-    if (!__ballot(i < c1)) break;
-    if (i < c1) {
-      const int e = key_expert(pool[i], base);
+  for (int i = 0; i < PP; ++i) {
+    if (!__ballot(i < n)) break;
+    if (i < n) {
+      const int e = key_expert(pl[i], c, sub);
       const uint32_t o = ord_f32(sigmoid_rn32(row[e]) + bias_g[e]);
       t2 = umax(t2, umin(t1, o));
       t1 = umax(t1, o);
     }
   }
   top2_merge(t1, t2, dpp<DPP_XOR1>(t1), dpp<DPP_XOR1>(t2));
-  const float gsx = (p.topn == 2) ? ord_inv(t1) + ord_inv(t2) : ord_inv(t1);
-  const uint64_t gkx = ((uint64_t)ord_f32(gsx) << 3) | (uint64_t)(7 - g);
-  const bool kept = group_rank(gkx) < p.TG;
+  top2_merge(t1, t2, dpp<DPP_XOR2>(t1), dpp<DPP_XOR2>(t2));
+}
+
+// Exact refinement of the rows with `need` set (call with the whole wave).
+// Exact group scores come from every
+// pool entry that can hold a group's top scores; then the exact top_k from
+// every kept-pool entry within twice the key error of the (top_k+1)-th
+// extracted key. Both steps decide on exact scores, so they only fail when
+// a pool is too short or the candidates exceed MAX_CAND. Returns true
+// (row-uniform) when the row has been written.
+__device__ __forceinline__ bool refine_rows(const float *__restrict__ row,
+                                            const float *__restrict__ bias_g,
+                                            const uint32_t (&a)[PP], const uint32_t (&b)[PP],
+                                            bool need, const RouteParams &p, int r, int u,
+                                            int64_t t, RowScratch *L, int32_t *__restrict__ ids,
+                                            float *__restrict__ wts,
+                                            int32_t *__restrict__ packed) {
+  const int K = p.K;
+  const int c = u >> 2, sub = u & 3;
+  if (need && u == 0) atomicAdd(&g_refined_tokens, 1ull);
+
+  // ---- exact group scores ------------------------------------------------------
+  // An expert whose key value is below thr is beaten, even exactly, by the
+  // two experts holding its group's approximate top-2 keys.
+  uint32_t a1 = a[0], a2 = a[1], b1 = b[0], b2 = b[1];
+  top2_merge(a1, a2, dpp<DPP_XOR1>(a1), dpp<DPP_XOR1>(a2));
+  top2_merge(a1, a2, dpp<DPP_XOR2>(a1), dpp<DPP_XOR2>(a2));
+  top2_merge(b1, b2, dpp<DPP_XOR1>(b1), dpp<DPP_XOR1>(b2));
+  top2_merge(b1, b2, dpp<DPP_XOR2>(b1), dpp<DPP_XOR2>(b2));
+  const double thra = (double)key_v(p.topn == 2 ? a2 : a1) - 2.0 * (double)row_err(key_v(a1));
+  const double thrb = (double)key_v(p.topn == 2 ? b2 : b1) - 2.0 * (double)row_err(key_v(b1));
+  const int na = need ? pool_count_ge(a, thra) : 0;
+  const int nb = need ? pool_count_ge(b, thrb) : 0;
+  bool fail = row_max((na >= PP || nb >= PP) ? 1u : 0u) != 0u;
+  uint32_t ta1, ta2, tb1, tb2;
+  exact_top2(row, bias_g, a, na, c, sub, ta1, ta2);
+  exact_top2(row, bias_g, b, nb, c, sub, tb1, tb2);
+  const float gxa = (p.topn == 2) ? ord_inv(ta1) + ord_inv(ta2) : ord_inv(ta1);
+  const float gxb = (p.topn == 2) ? ord_inv(tb1) + ord_inv(tb2) : ord_inv(tb1);
+  int ra, rb;
+  group_ranks(((uint64_t)ord_f32(gxa) << 3) | (uint64_t)(7 - c),
+              ((uint64_t)ord_f32(gxb) << 3) | (uint64_t)(3 - c), ra, rb);
+  const bool kept_a = ra < p.TG, kept_b = rb < p.TG;
 
   // ---- extraction over the exactly kept groups ----------------------------------
-  uint32_t q[POOL];
-#pragma unroll
-  for (int i = 0; i < POOL; ++i) q[i] = pool[i];
-  q[0] = kept ? q[0] : 0u;
-  uint32_t M = 0u;
-  for (int rd = 0; rd <= K; ++rd) {
-    M = row_max(q[0]);
-    const bool win = q[0] == M;
-#pragma unroll
-    for (int i = 0; i < POOL - 1; ++i) q[i] = win ? q[i + 1] : q[i];
-  }
+  uint32_t m[POOL];
+  merge_kept(a, b, kept_a, kept_b, m);
+  uint32_t rounds;
+  const uint32_t M = extract(m, K, rounds);
 
   // ---- exact top_k from the candidates within the error band ----------------------
   const float vm = key_v(M);
   const double thb = (double)vm - 2.0 * (double)row_err(vm);
-  const int c2 = (need && kept) ? pool_count_ge(pool, thb) : 0;
-  fail = fail || row_max(c2 >= POOL ? 1u : 0u) != 0u;
-  const int m = (int)row_sum((uint32_t)c2);
-  fail = fail || m > MAX_CAND || m < K;
+  const int ca = (need && kept_a) ? pool_count_ge(a, thb) : 0;
+  const int cb = (need && kept_b) ? pool_count_ge(b, thb) : 0;
+  fail = fail || row_max((ca >= PP || cb >= PP) ? 1u : 0u) != 0u;
+  const int c2 = ca + cb;
+  const int mc = (int)row_sum((uint32_t)c2);
+  fail = fail || mc > MAX_CAND || mc < K;
   L->cnt[r][u] = c2;
   wave_lds_sync();
   int excl = 0;
 #pragma unroll
   for (int j = 0; j < LANES; ++j) excl += (j < u) ? L->cnt[r][j] : 0;
 #pragma unroll
-  for (int i = 0; i < POOL; ++i) {
-    if (!__ballot(i < c2)) break;
-    if (i < c2 && excl + i < MAX_CAND) L->cand[r][excl + i] = key_expert(pool[i], base);
+  for (int i = 0; i < PP; ++i) {
+    if (!__ballot(i < ca || i < cb)) break;
+    if (i < ca && excl + i < MAX_CAND) L->cand[r][excl + i] = key_expert(a[i], c, sub);
+    if (i < cb && excl + ca + i < MAX_CAND)
+      L->cand[r][excl + ca + i] = key_expert(b[i], c, sub);
   }
   wave_lds_sync();
   const bool ok_m = need && !fail;
@@ -281,7 +417,7 @@ __device__ __forceinline__ bool refine_rows(const float *__restrict__ row,
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int j = u + LANES * h;
-    if (ok_m && j < m) {
+    if (ok_m && j < mc) {
       eid[h] = L->cand[r][j];
       es[h] = sigmoid_rn32(row[eid[h]]);
       const float sp = es[h] + bias_g[eid[h]];
@@ -290,17 +426,17 @@ __device__ __forceinline__ bool refine_rows(const float *__restrict__ row,
     }
   }
   wave_lds_sync();
-  const int mmax = (int)wave_max_u32(ok_m ? (uint32_t)m : 0u);
+  const int mmax = (int)wave_max_u32(ok_m ? (uint32_t)mc : 0u);
   int rk[2] = {0, 0};
   for (int j = 0; j < mmax; ++j) {
-    const uint64_t o = (ok_m && j < m) ? L->ekey[r][j] : 0ull;
+    const uint64_t o = (ok_m && j < mc) ? L->ekey[r][j] : 0ull;
     rk[0] += o > ek[0] ? 1 : 0;
     rk[1] += o > ek[1] ? 1 : 0;
   }
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int j = u + LANES * h;
-    if (ok_m && j < m && rk[h] < K) {
+    if (ok_m && j < mc && rk[h] < K) {
       L->slot[r][rk[h]] = make_uint2((uint32_t)eid[h], __float_as_uint(es[h]));
       if (rk[h] == K - 1) L->kth[r] = ord_inv((uint32_t)(ek[h] >> 32));
     }
@@ -329,105 +465,44 @@ __device__ __forceinline__ uint32_t route_rows4(const float *__restrict__ logits
                                                 int32_t *__restrict__ packed) {
   int ln = lane;
   asm volatile("" : "+v"(ln));
-  const int r = ln >> 4, u = ln & 15, g = u >> 1, sub = u & 1;
+  const int r = ln >> 4, u = ln & 15, c = u >> 2, sub = u & 3;
   const int64_t t = t0 + r;
   const bool valid = t < T;
   const float *row = logits + (size_t)(valid ? t : (int64_t)T - 1) * E;
-  const int base = g * EG + 4 * sub;
-  const float4 *xp = reinterpret_cast<const float4 *>(row + base);
-  const float4 *bp = reinterpret_cast<const float4 *>(bias_lds + g * BIAS_GSTRIDE + 4 * sub);
-
-  // ---- streaming: keys -> the lane's top-7 ----------------------------------
-  // Loads run PREFETCH float4 ahead of their use.
-  uint32_t p1 = 0u, p2 = 0u, p3 = 0u, p4 = 0u, p5 = 0u, p6 = 0u, p7 = 0u, p8 = 0u, p9 = 0u,
-           p10 = 0u;
-  constexpr int PREFETCH = 3;
-  float4 xq[PREFETCH];
-#pragma unroll
-  for (int i = 0; i < PREFETCH; ++i) xq[i] = xp[2 * i];
-#pragma unroll
-  for (int i = 0; i < NQ; ++i) {
-    const float4 xv = xq[i % PREFETCH];
-    if (i + PREFETCH < NQ) xq[i % PREFETCH] = xp[2 * (i + PREFETCH)];
-    const float4 bv = bp[2 * i];
-    const float xs[4] = {xv.x, xv.y, xv.z, xv.w};
-    const float bs[4] = {bv.x, bv.y, bv.z, bv.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float v = fast_sigmoid(xs[j]) + bs[j];
-      const uint32_t k = (__float_as_uint(v) << 6) | (uint32_t)(63 - (4 * i + j));
-      p10 = umed3(p9, p10, k);
-      p9 = umed3(p8, p9, k);
-      p8 = umed3(p7, p8, k);
-      p7 = umed3(p6, p7, k);
-      p6 = umed3(p5, p6, k);
-      p5 = umed3(p4, p5, k);
-      p4 = umed3(p3, p4, k);
-      p3 = umed3(p2, p3, k);
-      p2 = umed3(p1, p2, k);
-      p1 = umax(p1, k);
-    }
-    // materialise the pool here: otherwise the compiler sinks the lower
-    // pool levels to the end and keeps every intermediate key alive
-    asm volatile("" : "+v"(p1), "+v"(p2), "+v"(p3), "+v"(p4), "+v"(p5), "+v"(p6), "+v"(p7),
-                 "+v"(p8), "+v"(p9), "+v"(p10));
-  }
-
-  // ---- groups ---------------------------------------------------------------
-  const uint32_t o1 = dpp<DPP_XOR1>(p1), o2 = dpp<DPP_XOR1>(p2);
-  const uint32_t m1 = umax(p1, o1);
-  const uint32_t m2 = umax(umax(umin(p1, o1), p2), o2);
-  const float gs = (p.topn == 2) ? key_v(m1) + key_v(m2) : key_v(m1);  // in [2, 1030)
-  // unique group key: score bits (the top 3 bits are constant), then lower group
-  const uint32_t gk = (__float_as_uint(gs) << 3) | (uint32_t)(7 - g);
-  const bool kept = group_rank(gk) < p.TG;
-  // certified when the weakest kept group beats the strongest dropped one
-  // by more than both error bounds
-  const uint32_t gsb = __float_as_uint(gs);
-  const float kmin = __uint_as_float(row_min(kept ? gsb : 0x7F7FFFFFu));
-  const float dmax = __uint_as_float(row_max(kept ? 0u : gsb));
-  bool fail = !(kmin - row_group_err(kmin) > dmax + row_group_err(dmax));
-
-  // ---- extraction: top_k + 1 rounds of row maximum ---------------------------
-  const uint32_t pool[POOL] = {p1, p2, p3, p4, p5, p6, p7, p8, p9, p10};
-  p1 = kept ? p1 : 0u;  // dropped lanes never win (real keys are > 0 unless v == 2)
-  const uint32_t s1 = p1, s2 = p2, s3 = p3, s4 = p4, s5 = p5, s6 = p6, s7 = p7, s8 = p8, s9 = p9;
-  uint32_t rounds = 0u;  // bit (K - round) set when this lane won that round
-  uint32_t M = 0u;       // after the loop: the (K+1)-th key, the best non-winner
   const int K = p.K;
-  for (int rd = 0; rd <= K; ++rd) {
-    M = row_max(p1);
-    const bool win = p1 == M;
-    rounds = rounds + rounds + (win ? 1u : 0u);
-    p1 = win ? p2 : p1;
-    p2 = win ? p3 : p2;
-    p3 = win ? p4 : p3;
-    p4 = win ? p5 : p4;
-    p5 = win ? p6 : p5;
-    p6 = win ? p7 : p6;
-    p7 = win ? p8 : p7;
-    p8 = win ? p9 : p8;
-    p9 = win ? p10 : p9;
-  }
+
+  // ---- streaming, groups, merged pool, extraction -----------------------------
+  uint32_t a[PP], b[PP];
+  stream_pools(row, bias_lds, c, sub, a, b);
+  bool kept_a, kept_b;
+  bool fail = !approx_groups(a, b, p, c, kept_a, kept_b);
+  uint32_t m[POOL];
+  merge_kept(a, b, kept_a, kept_b, m);
+  uint32_t rounds;
+  const uint32_t M = extract(m, K, rounds);
   const int pops = __popc(rounds);
   const uint32_t total = row_sum((uint32_t)pops);
-  // exactly K+1 entries taken (no equal keys) and no lane used up its pool
+  // exactly K+1 entries taken (no equal keys) and the merged pool not used up
   fail = fail || total != (uint32_t)(K + 1) || pops >= POOL;
 
   // ---- winners (the first K extracted) to LDS: expert ids ----------------------
   uint32_t rem = rounds >> 1;  // drop round K (the best non-winner)
+  int pa = 0, pb = 0;          // popped entries of each pass (round K included)
 #pragma unroll
   for (int i = 0; i < POOL - 1; ++i) {
-    if (!__ballot(rem != 0u)) break;
-    if (rem != 0u) {
-      const uint32_t key = i == 0 ? s1 : i == 1 ? s2 : i == 2 ? s3 : i == 3 ? s4 : i == 4 ? s5
-                         : i == 5 ? s6 : i == 6 ? s7 : i == 7 ? s8 : s9;
-      const int hb = 31 - __clz(rem);  // earliest remaining round
-      rem ^= 1u << hb;
-      const int q = 63 - (int)(key & 63u);
-      L->id[r][K - 1 - hb] = base + q + (q & ~3);
+    if (!__ballot(i < pops)) break;
+    if (i < pops) {
+      const uint32_t key = m[i];
+      if (key_pass1(key)) ++pb; else ++pa;
+      if (rem != 0u) {
+        const int hb = 31 - __clz(rem);  // earliest remaining round
+        rem ^= 1u << hb;
+        L->id[r][K - 1 - hb] = key_expert(key, c, sub);
+      }
     }
   }
+  // a pass pool used up may hide further keys of that group
+  fail = fail || pa >= PP || pb >= PP;
   wave_lds_sync();
 
   // ---- exact scores of the winners; exact order by (sp desc, id asc) ---------------
@@ -446,8 +521,7 @@ __device__ __forceinline__ uint32_t route_rows4(const float *__restrict__ logits
   const float vm = key_v(M);
   const double bound = (double)vm - 3.0 + (double)row_err(vm);
   const uint32_t weakest = row_min(act ? ord_f32(my_sp) : 0xFFFFFFFFu);
-  const float wsp = __uint_as_float((weakest & 0x80000000u) ? (weakest & 0x7FFFFFFFu) : ~weakest);
-  const bool boundary_ok = (double)wsp > bound;
+  const bool boundary_ok = (double)ord_inv(weakest) > bound;
   wave_lds_sync();
   int rank = 0;
   if (act) {
@@ -456,9 +530,7 @@ __device__ __forceinline__ uint32_t route_rows4(const float *__restrict__ logits
   }
   const uint32_t row_fail = pre_fail | ((valid && !boundary_ok && pre_fail == 0u) ? 1u : 0u);
 
-  // ---- epilogue: lane u takes slot u (the winner of exact rank u); weights,
-  // relabel, pack, store with the same arithmetic, in the same order, as the
-  // one-token-per-wave epilogue, so both paths give identical bits
+  // ---- epilogue: lane u takes slot u (the winner of exact rank u) ----------------
   if (row_fail == 0u && act) L->slot[r][rank] = make_uint2((uint32_t)my_id, __float_as_uint(my_s));
   wave_lds_sync();
   const bool out = row_fail == 0u && act;
@@ -471,8 +543,7 @@ __device__ __forceinline__ uint32_t route_rows4(const float *__restrict__ logits
   const bool need = !done && valid;
   if (__ballot(need)) {
     wave_lds_sync();
-    done = refine_rows(row, bias_g, pool, m1, m2, need, p, r, u, g, base, t, L, ids, wts, packed) ||
-           done;
+    done = refine_rows(row, bias_g, a, b, need, p, r, u, t, L, ids, wts, packed) || done;
   }
   // rows to route again
   const uint64_t fb = __ballot(!done && valid && u == 0);
