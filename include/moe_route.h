@@ -97,10 +97,11 @@ int32_t moe_route_local_num_experts(int32_t num_experts, int32_t top_k,
 
 /*
  * Workspace bytes needed by moe_route / moe_route_local for `num_tokens`
- * tokens and `num_experts_out` output ids (E'). The first 256 bytes are a
- * control block that must be zero before the workspace is first used; every
- * call leaves it zero again. One workspace must not be used by two calls
- * that can run at the same time.
+ * tokens and `num_experts_out` output ids (E'): a 256-byte control block
+ * and, above 64 tokens, the permutation's per-block id counts and in-block
+ * ranks. The control block must be zero before the workspace is first used;
+ * every call leaves it zero again. The rest needs no initial contents. One
+ * workspace must not be used by two calls that can run at the same time.
  */
 size_t moe_route_workspace_bytes(int32_t num_tokens, int32_t num_experts_out,
                                  int32_t top_k);
@@ -132,8 +133,9 @@ int moe_route_local(const float *logits, const float *bias,
                     size_t workspace_bytes, void *stream);
 
 /*
- * Workspace bytes needed by moe_router_gemm_route (router GEMM staging plus
- * the routing workspace).
+ * Workspace bytes needed by moe_router_gemm_route: the routing workspace
+ * first (moe_route_workspace_bytes, same control-block rule), then the
+ * router GEMM's split-K partial sums.
  */
 size_t moe_router_gemm_route_workspace_bytes(int32_t num_tokens, int32_t hidden,
                                              int32_t num_experts,

@@ -1,20 +1,19 @@
 // moe_route.hip - routing kernels for gfx950 and the C ABI of include/moe_route.h.
 //
-// Paths (both give identical results):
+// Paths (all give identical results):
 //  * decode, T <= 64: ONE launch. Blocks of 4 waves route one token per wave
 //    and publish their outputs; the last block to arrive (ticket in the
 //    workspace control block) builds counts, offsets and the permutation from
 //    per-expert 64-bit token masks in LDS.
-//  * prefill, T > 64: four launches.
-//      route_tokens: one token per wave, waves independent (no barriers), so
-//                    the per-token latency is hidden by occupancy alone.
-//      tile_count:   tiles of 64 tokens: a 64-bit token mask per output id in
-//                    LDS gives the tile histogram hist[e'][tile] and each
-//                    entry's rank among the tile's entries of the same id.
-//      tile_prefix:  per output id, exclusive scan of hist[e'][:] over tiles;
-//                    total -> counts[e'].
-//      scatter:      offsets = exclusive scan of counts; each entry goes to
-//                    offsets[e'] + hist[e'][tile] + rank_in_tile.
+//  * prefill, T > 64: three launches.
+//      route:   four tokens per wave (896 experts in 8 groups, route_rows.hpp)
+//               or one token per wave (other shapes); at the end of every
+//               block, per output id the block's entry count -> hist[e'][blk]
+//               and per entry its rank within the block -> rank8.
+//      prefix:  per output id, exclusive scan of hist[e'][:] over blocks;
+//               total -> counts[e'].
+//      scatter: offsets = exclusive scan of counts; each entry goes to
+//               offsets[e'] + hist[e'][blk] + rank8[f].
 // Within one token the output ids are distinct (top-k ids are distinct and
 // the relabelled ids are unique per row), so "ascending flat index within an
 // expert" is "ascending token", and a token's position among the entries of
@@ -35,9 +34,6 @@ namespace moe {
 constexpr int WAVES_PER_BLOCK = 4;
 constexpr int BLOCK = 64 * WAVES_PER_BLOCK;
 constexpr size_t CONTROL_BYTES = 256;
-// Prefill tiles of the permutation: 64 tokens (token masks are 64-bit).
-constexpr int TILE_TOKENS = 64;
-
 // Exclusive scan of in[0..n) (n <= 1024, any memory) into out[0..n] in LDS,
 // out[n] = total. All BLOCK threads must call it.
 __device__ void block_exclusive_scan(const int32_t *in, int n, int32_t *out, int32_t *wave_tot) {
@@ -70,6 +66,42 @@ __device__ void block_exclusive_scan(const int32_t *in, int n, int32_t *out, int
   }
   if (tid == BLOCK - 1) out[n] = wave_off + incl;
   __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// Prefill permutation, part 1 (end of every prefill route block, all BLOCK
+// threads, after the block's outputs are written): per output id, the
+// block's entry count -> hist[e'][block]; per entry, its rank among the
+// block's entries of the same id (token order) -> rank8[f]. Plain stores of
+// every value, so the workspace needs no initial contents. A block covers at
+// most 32 tokens (32-bit token masks in LDS).
+// ---------------------------------------------------------------------------
+__device__ void block_counts(const int32_t *__restrict__ packed, int K, int e_out, int64_t t_begin,
+                             int ntok, int blk, int nblk, int32_t *__restrict__ hist,
+                             uint8_t *__restrict__ rank8, uint32_t *lds_mask) {
+  const int tid = threadIdx.x;
+  __syncthreads();  // every wave done (lds_mask may share LDS with routing scratch)
+  for (int e = tid; e < e_out; e += BLOCK) lds_mask[e] = 0u;
+  __syncthreads();  // also orders this block's output stores before the reads below
+  const int n = ntok * K;
+  const int32_t *pk = packed + t_begin * K;
+  int ev[2], tv[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = tid + h * BLOCK;
+    if (i < n) {
+      ev[h] = pk[i] >> 16;
+      tv[h] = i / K;
+      atomicOr(&lds_mask[ev[h]], 1u << tv[h]);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = tid + h * BLOCK;
+    if (i < n) rank8[t_begin * K + i] = (uint8_t)__popc(lds_mask[ev[h]] & ((1u << tv[h]) - 1u));
+  }
+  for (int e = tid; e < e_out; e += BLOCK) hist[(size_t)e * nblk + blk] = __popc(lds_mask[e]);
 }
 
 // ---------------------------------------------------------------------------
@@ -131,106 +163,111 @@ __global__ __launch_bounds__(BLOCK) void route_decode_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Prefill path, kernel 1: route tiles of 64 tokens.
+// Prefill path, kernel 1 (any shape): one token per wave, then the block's
+// share of the tile counts (prefill_tile_counts).
 // ---------------------------------------------------------------------------
+struct PrefillCounts {
+  int32_t *hist;      // [e_out][route blocks]
+  uint8_t *rank8;     // [T * K]
+};
+
 template <int NP, int LPG>
 __global__ __launch_bounds__(BLOCK) void route_tokens_kernel(
     const float *__restrict__ logits, const float *__restrict__ bias, int T, RouteParams p,
-    int32_t *__restrict__ ids, float *__restrict__ wts, int32_t *__restrict__ packed) {
-  __shared__ WaveScratch scratch[WAVES_PER_BLOCK];
+    int32_t *__restrict__ ids, float *__restrict__ wts, int32_t *__restrict__ packed,
+    PrefillCounts pc) {
+  // routing scratch, reused for the tile counts once every wave is done
+  __shared__ union {
+    WaveScratch wave[WAVES_PER_BLOCK];
+    uint32_t mask[MOE_ROUTE_MAX_EXPERTS];
+  } lds;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  const int t = blockIdx.x * WAVES_PER_BLOCK + wave;
-  if (t >= T) return;
-  const float *row = logits + (size_t)t * p.E;
-  float b[2 * NP], x[2 * NP];
-  load_lane_layout<NP, LPG>(row, p, lane, x);
-  load_lane_layout<NP, LPG>(bias, p, lane, b);
-  route_token<NP, LPG>(row, x, b, bias, p, lane, t, &scratch[wave], ids, wts, packed);
+  const int64_t tb = (int64_t)blockIdx.x * WAVES_PER_BLOCK;
+  const int64_t t = tb + wave;
+  if (t < T) {
+    const float *row = logits + (size_t)t * p.E;
+    float b[2 * NP], x[2 * NP];
+    load_lane_layout<NP, LPG>(row, p, lane, x);
+    load_lane_layout<NP, LPG>(bias, p, lane, b);
+    route_token<NP, LPG>(row, x, b, bias, p, lane, t, &lds.wave[wave], ids, wts, packed);
+  }
+  block_counts(packed, p.K, p.e_out, tb, (int)min((int64_t)WAVES_PER_BLOCK, T - tb), blockIdx.x,
+               gridDim.x, pc.hist, pc.rank8, lds.mask);
 }
 
 // Prefill path, kernel 1 for the 896-expert, 8-group shape: four tokens per
 // wave (route_rows.hpp); rows that fail their certificate are routed again
-// one token per wave.
+// one token per wave. Then the block's share of the tile counts.
 __device__ unsigned long long g_row_fallback_tokens = 0ull;
+
+constexpr int ROWS_TOKENS_PER_BLOCK = 4 * WAVES_PER_BLOCK;
+static_assert(ROWS_TOKENS_PER_BLOCK <= 32 && WAVES_PER_BLOCK <= 32, "32-bit token masks");
 
 __global__ __launch_bounds__(BLOCK, 8) void route_rows_kernel(
     const float *__restrict__ logits, const float *__restrict__ bias, int T, RouteParams p,
-    int32_t *__restrict__ ids, float *__restrict__ wts, int32_t *__restrict__ packed) {
+    int32_t *__restrict__ ids, float *__restrict__ wts, int32_t *__restrict__ packed,
+    PrefillCounts pc) {
   __shared__ float bias_lds[rows::E];
+  // routing scratch, reused for the tile counts once every wave is done
   __shared__ union {
-    rows::RowScratch r;
-    WaveScratch w;
-  } scratch[WAVES_PER_BLOCK];
+    union {
+      rows::RowScratch r;
+      WaveScratch w;
+    } wave[WAVES_PER_BLOCK];
+    uint32_t mask[MOE_ROUTE_MAX_EXPERTS];
+  } lds;
   __shared__ int bad_bias;
-  const bool ok = rows::stage_bias<BLOCK>(bias, bias_lds, &bad_bias);  // all threads, before any exit
+  const bool ok = rows::stage_bias<BLOCK>(bias, bias_lds, &bad_bias);  // all threads
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  const int64_t t0 = ((int64_t)blockIdx.x * WAVES_PER_BLOCK + wave) * 4;
-  if (t0 >= T) return;
-  uint32_t redo = 0xFu;
-  if (ok)
-    redo = rows::route_rows4(logits, bias, bias_lds, T, t0, p, lane, &scratch[wave].r, ids, wts,
-                             packed);
-  redo = (uint32_t)__builtin_amdgcn_readfirstlane((int)redo);
-  while (redo) {
-    const int r = __builtin_ctz(redo);
-    redo &= redo - 1u;
-    const int64_t t = t0 + r;
-    if (t >= T) break;
-    if (lane == 0) atomicAdd(&g_row_fallback_tokens, 1ull);
-    const float *row = logits + (size_t)t * p.E;
-    float b[14], x[14];
-    load_lane_layout<7, 8>(row, p, lane, x);
-    load_lane_layout<7, 8>(bias, p, lane, b);
-    route_token<7, 8>(row, x, b, bias, p, lane, t, &scratch[wave].w, ids, wts, packed,
-                      /*fast_first=*/false);
+  const int64_t tb = (int64_t)blockIdx.x * ROWS_TOKENS_PER_BLOCK;
+  const int64_t t0 = tb + 4 * wave;
+  if (t0 < T) {
+    uint32_t redo = 0xFu;
+    if (ok)
+      redo = rows::route_rows4(logits, bias, bias_lds, T, t0, p, lane, &lds.wave[wave].r, ids,
+                               wts, packed);
+    redo = (uint32_t)__builtin_amdgcn_readfirstlane((int)redo);
+    while (redo) {
+      const int r = __builtin_ctz(redo);
+      redo &= redo - 1u;
+      const int64_t t = t0 + r;
+      if (t >= T) break;
+      if (lane == 0) atomicAdd(&g_row_fallback_tokens, 1ull);
+      const float *row = logits + (size_t)t * p.E;
+      float b[14], x[14];
+      load_lane_layout<7, 8>(row, p, lane, x);
+      load_lane_layout<7, 8>(bias, p, lane, b);
+      route_token<7, 8>(row, x, b, bias, p, lane, t, &lds.wave[wave].w, ids, wts, packed,
+                        /*fast_first=*/false);
+    }
   }
+  block_counts(packed, p.K, p.e_out, tb, (int)min((int64_t)ROWS_TOKENS_PER_BLOCK, T - tb),
+               blockIdx.x, gridDim.x, pc.hist, pc.rank8, lds.mask);
 }
 
-// Prefill path, kernel 1b: per tile of TILE_TOKENS tokens, a 64-bit token
-// mask per output id (in LDS) gives the tile histogram hist[e'][tile] and
-// each entry's rank among the tile's entries of the same id.
-__global__ __launch_bounds__(BLOCK) void tile_count_kernel(const int32_t *__restrict__ packed,
-                                                           int T, int K, int e_out,
-                                                           int32_t *__restrict__ hist, int ntiles,
-                                                           int32_t *__restrict__ tile_rank) {
-  __shared__ unsigned long long mask[MOE_ROUTE_MAX_EXPERTS];
-  const int tile = blockIdx.x;
-  const int nt = min(TILE_TOKENS, T - tile * TILE_TOKENS);
-  const int n = nt * K;
-  const int32_t *pk = packed + (size_t)tile * TILE_TOKENS * K;
-  for (int i = threadIdx.x; i < e_out; i += BLOCK) mask[i] = 0ull;
-  __syncthreads();
-  for (int q = threadIdx.x; q < n; q += BLOCK) atomicOr(&mask[pk[q] >> 16], 1ull << (q / K));
-  __syncthreads();
-  for (int i = threadIdx.x; i < e_out; i += BLOCK)
-    hist[(size_t)i * ntiles + tile] = __popcll(mask[i]);
-  int32_t *tr = tile_rank + (size_t)tile * TILE_TOKENS * K;
-  for (int q = threadIdx.x; q < n; q += BLOCK)
-    tr[q] = __popcll(mask[pk[q] >> 16] & ((1ull << (q / K)) - 1ull));
-}
+// Prefill permutation, part 2: one block per output id: exclusive scan of
+// hist[e'][0..nblk) in place (entries of e' in earlier route blocks) and the
+// id's total -> counts[e'].
+constexpr int SCAN_PER_THREAD = 8;
 
-// Prefill path, kernel 2: per output id, exclusive scan over tiles (in
-// place) and the id's total -> counts. One block per id; each thread scans a
-// contiguous run of PREFIX_RUN tiles, so a wave reads 2 KB contiguously.
-constexpr int PREFIX_RUN = 8;
-__global__ __launch_bounds__(BLOCK) void tile_prefix_kernel(int32_t *__restrict__ hist, int ntiles,
-                                                            int32_t *__restrict__ counts) {
+__global__ __launch_bounds__(BLOCK) void block_prefix_kernel(int32_t *__restrict__ hist, int nblk,
+                                                             int32_t *__restrict__ counts) {
   __shared__ int32_t wave_tot[WAVES_PER_BLOCK];
-  int32_t *row = hist + (size_t)blockIdx.x * ntiles;
+  int32_t *row = hist + (size_t)blockIdx.x * nblk;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   int carry = 0;
-  for (int base = 0; base < ntiles; base += BLOCK * PREFIX_RUN) {
-    const int beg = base + tid * PREFIX_RUN;
-    int v[PREFIX_RUN];
-    int s = 0;
+  for (int base = 0; base < nblk; base += BLOCK * SCAN_PER_THREAD) {
+    const int beg = base + tid * SCAN_PER_THREAD;
+    int v[SCAN_PER_THREAD];
+    int sum = 0;
 #pragma unroll
-    for (int k = 0; k < PREFIX_RUN; ++k) {
-      v[k] = (beg + k < ntiles) ? row[beg + k] : 0;
-      s += v[k];
+    for (int k = 0; k < SCAN_PER_THREAD; ++k) {
+      v[k] = (beg + k < nblk) ? row[beg + k] : 0;
+      sum += v[k];
     }
-    int incl = s;
+    int incl = sum;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
       const int o = __shfl_up(incl, d);
@@ -238,17 +275,16 @@ __global__ __launch_bounds__(BLOCK) void tile_prefix_kernel(int32_t *__restrict_
     }
     if (lane == 63) wave_tot[wv] = incl;
     __syncthreads();
-    int off = carry;
-    int total = 0;
+    int off = carry, total = 0;
 #pragma unroll
     for (int w = 0; w < WAVES_PER_BLOCK; ++w) {
       if (w < wv) off += wave_tot[w];
       total += wave_tot[w];
     }
-    int run = off + incl - s;
+    int run = off + incl - sum;
 #pragma unroll
-    for (int k = 0; k < PREFIX_RUN; ++k) {
-      if (beg + k < ntiles) row[beg + k] = run;
+    for (int k = 0; k < SCAN_PER_THREAD; ++k) {
+      if (beg + k < nblk) row[beg + k] = run;
       run += v[k];
     }
     carry += total;
@@ -257,24 +293,45 @@ __global__ __launch_bounds__(BLOCK) void tile_prefix_kernel(int32_t *__restrict_
   if (tid == 0) counts[blockIdx.x] = carry;
 }
 
-// Prefill path, kernel 3: scatter every entry to its expert-major position.
+// Prefill permutation, part 3: offsets = exclusive scan of counts (every
+// block forms it in LDS; block 0 writes it out), then every entry f goes to
+// offsets[e'] + hist[e'][its route block] + rank8[f]. A thread takes
+// SCATTER_PER_THREAD entries and issues each round of loads for all of them
+// before using any.
+constexpr int SCATTER_PER_THREAD = 4;
+
 __global__ __launch_bounds__(BLOCK) void scatter_kernel(
-    const int32_t *__restrict__ packed, const int32_t *__restrict__ tile_rank,
-    const int32_t *__restrict__ hist, int ntiles, const int32_t *__restrict__ counts, int e_out,
-    int64_t n, int K, int tile_tokens, int32_t *__restrict__ offsets,
+    const int32_t *__restrict__ packed, const int32_t *__restrict__ hist,
+    const uint8_t *__restrict__ rank8, const int32_t *__restrict__ counts, int e_out, int nblk,
+    int tokens_per_blk, int K, int64_t n, int32_t *__restrict__ offsets,
     int32_t *__restrict__ perm, int32_t *__restrict__ inv) {
   __shared__ int32_t offs[MOE_ROUTE_MAX_EXPERTS + 1];
   __shared__ int32_t wave_tot[WAVES_PER_BLOCK];
+  const int64_t f0 = (int64_t)blockIdx.x * BLOCK * SCATTER_PER_THREAD + threadIdx.x;
+  int ev[SCATTER_PER_THREAD], rv[SCATTER_PER_THREAD];
+#pragma unroll
+  for (int k = 0; k < SCATTER_PER_THREAD; ++k) {
+    const int64_t f = f0 + (int64_t)k * BLOCK;
+    ev[k] = f < n ? packed[f] >> 16 : 0;
+    rv[k] = f < n ? rank8[f] : 0;
+  }
+  int hv[SCATTER_PER_THREAD];
+#pragma unroll
+  for (int k = 0; k < SCATTER_PER_THREAD; ++k) {
+    const int64_t f = f0 + (int64_t)k * BLOCK;
+    hv[k] = f < n ? hist[(size_t)ev[k] * nblk + (int)((f / K) / tokens_per_blk)] : 0;
+  }
   block_exclusive_scan(counts, e_out, offs, wave_tot);
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i <= e_out; i += BLOCK) offsets[i] = offs[i];
-  for (int64_t f = (int64_t)blockIdx.x * BLOCK + threadIdx.x; f < n;
-       f += (int64_t)gridDim.x * BLOCK) {
-    const int e = packed[f] >> 16;
-    const int tile = (int)((f / K) / tile_tokens);
-    const int pos = offs[e] + hist[(size_t)e * ntiles + tile] + tile_rank[f];
-    perm[pos] = (int32_t)f;
-    if (inv) inv[f] = pos;
+#pragma unroll
+  for (int k = 0; k < SCATTER_PER_THREAD; ++k) {
+    const int64_t f = f0 + (int64_t)k * BLOCK;
+    if (f < n) {
+      const int32_t pos = offs[ev[k]] + hv[k] + rv[k];
+      perm[pos] = (int32_t)f;
+      if (inv) inv[f] = pos;
+    }
   }
 }
 
@@ -307,20 +364,20 @@ static int validate_params(const moe_route_params *prm) {
   return MOE_OK;
 }
 
-static int ntiles_for(int T) { return (T + TILE_TOKENS - 1) / TILE_TOKENS; }
-
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
-
-static int cu_count();
 
 // Benchmark hook (moe_route_set_kernel_events).
 static hipEvent_t g_ev_before = nullptr, g_ev_after = nullptr;
 
+// Workspace: the control block, then for the prefill path the per-route-
+// block id counts hist[e'][nblk] and the entries' in-block ranks. Sized for
+// the route kernel with the fewest tokens per block (one token per wave).
 static size_t route_ws_bytes(int T, int e_out, int K) {
   size_t b = CONTROL_BYTES;
   if (T > MOE_ROUTE_MAX_FUSED_TOKENS) {
-    b += align256((size_t)e_out * ntiles_for(T) * sizeof(int32_t));
-    b += align256((size_t)T * K * sizeof(int32_t));
+    const size_t nblk = ((size_t)T + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK;
+    b += align256(nblk * e_out * sizeof(int32_t));  // hist
+    b += align256((size_t)T * K);                    // rank8
   }
   return b;
 }
@@ -346,31 +403,27 @@ static hipError_t launch_route(const float *logits, const float *bias, int T, co
     if (g_ev_after) hipEventRecord(g_ev_after, st);
     return hipGetLastError();
   }
-  const int ntiles = ntiles_for(T);
-  int32_t *hist = reinterpret_cast<int32_t *>(ws + CONTROL_BYTES);
-  int32_t *tile_rank = reinterpret_cast<int32_t *>(
-      ws + CONTROL_BYTES + align256((size_t)rp.e_out * ntiles * sizeof(int32_t)));
-  const int cus = cu_count();
+  const bool rows_path = LPG == 8 && NP == 7 && rows_path_applies(rp, logits);
+  const int tpb = rows_path ? ROWS_TOKENS_PER_BLOCK : WAVES_PER_BLOCK;
+  const int nblk = (T + tpb - 1) / tpb;
+  PrefillCounts pc;
+  pc.hist = reinterpret_cast<int32_t *>(ws + CONTROL_BYTES);
+  pc.rank8 = reinterpret_cast<uint8_t *>(ws + CONTROL_BYTES +
+                                         align256((size_t)nblk * rp.e_out * sizeof(int32_t)));
   if (g_ev_before) hipEventRecord(g_ev_before, st);
-  if (LPG == 8 && NP == 7 && rows_path_applies(rp, logits)) {
-    const int nblk = (T + 4 * WAVES_PER_BLOCK - 1) / (4 * WAVES_PER_BLOCK);
+  if (rows_path) {
     route_rows_kernel<<<nblk, BLOCK, 0, st>>>(logits, bias, T, rp, o->topk_ids, o->topk_weights,
-                                              o->packed);
+                                              o->packed, pc);
   } else {
-    const int nblk = (T + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK;
     route_tokens_kernel<NP, LPG><<<nblk, BLOCK, 0, st>>>(logits, bias, T, rp, o->topk_ids,
-                                                     o->topk_weights, o->packed);
+                                                     o->topk_weights, o->packed, pc);
   }
   if (g_ev_after) hipEventRecord(g_ev_after, st);
-  tile_count_kernel<<<ntiles, BLOCK, 0, st>>>(o->packed, T, rp.K, rp.e_out, hist, ntiles,
-                                              tile_rank);
-  tile_prefix_kernel<<<rp.e_out, BLOCK, 0, st>>>(hist, ntiles, o->counts);
+  block_prefix_kernel<<<rp.e_out, BLOCK, 0, st>>>(pc.hist, nblk, o->counts);
   const int64_t n = (int64_t)T * rp.K;
-  int64_t g3 = (n + BLOCK * 4 - 1) / (BLOCK * 4);
-  if (g3 > 8 * cus) g3 = 8 * cus;
-  scatter_kernel<<<(int)g3, BLOCK, 0, st>>>(o->packed, tile_rank, hist, ntiles, o->counts,
-                                            rp.e_out, n, rp.K, TILE_TOKENS, o->offsets,
-                                            o->perm, o->inv_perm);
+  const int64_t g3 = (n + BLOCK * SCATTER_PER_THREAD - 1) / (BLOCK * SCATTER_PER_THREAD);
+  scatter_kernel<<<(int)g3, BLOCK, 0, st>>>(o->packed, pc.hist, pc.rank8, o->counts, rp.e_out,
+                                            nblk, tpb, rp.K, n, o->offsets, o->perm, o->inv_perm);
   return hipGetLastError();
 }
 
@@ -396,17 +449,6 @@ int validate_route_call(const float *logits, const float *bias, int32_t T,
   return MOE_OK;
 }
 
-static int cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int cus = 0;
-    hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    cached[dev] = cus > 0 ? cus : 256;
-  }
-  return cached[dev];
-}
 
 static int route_impl(const float *logits, const float *bias, int32_t T,
                       const moe_route_params *prm, int32_t off, int32_t cnt,

@@ -31,9 +31,14 @@ def run_case(case, check_ws=True):
                         group_topn=case.group_topn)
     torch.cuda.synchronize()
     if check_ws:
-        ws = M._WORKSPACES[DEV.index or 0]
-        assert int(ws[:256].count_nonzero()) == 0, "control block not left zeroed"
+        assert_workspace_zero()
     return to_numpy(out)
+
+
+def assert_workspace_zero():
+    """Every call must leave the workspace's control block zeroed."""
+    ws = M._WORKSPACES[DEV.index or 0]
+    assert int(ws[:256].count_nonzero()) == 0, "control block not left zeroed"
 
 
 def to_numpy(out):

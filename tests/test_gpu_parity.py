@@ -7,7 +7,7 @@ import torch
 import moe_expert_routing_amd as M
 import oracle as O
 import workloads as W
-from gpu_util import DEV, assert_parity, oracle_case, run_case, say, to_dev
+from gpu_util import DEV, assert_parity, assert_workspace_zero, oracle_case, run_case, say, to_dev
 
 pytestmark = [
     pytest.mark.gpu,
@@ -97,6 +97,7 @@ def test_router_gemm_then_route(T):
     wt = to_dev(c.weight.view(np.int16))
     out = M.router_gemm_route(hid, wt, to_dev(c.bias))
     torch.cuda.synchronize()
+    assert_workspace_zero()
     logits = out["logits"].cpu().numpy()
     ref = O.router_logits_ref(c.hidden, c.weight)
     bound = O.router_logits_bound(c.hidden, c.weight)
