@@ -18,6 +18,7 @@
 // the relabelled ids are unique per row), so "ascending flat index within an
 // expert" is "ascending token", and a token's position among the entries of
 // an id is a popcount of the id's token mask below it.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
@@ -76,19 +77,21 @@ __device__ void block_exclusive_scan(const int32_t *in, int n, int32_t *out, int
 // every value, so the workspace needs no initial contents. A block covers at
 // most 32 tokens (32-bit token masks in LDS).
 // ---------------------------------------------------------------------------
+template <int THREADS>
 __device__ void block_counts(const int32_t *__restrict__ packed, int K, int e_out, int64_t t_begin,
                              int ntok, int blk, int nblk, int32_t *__restrict__ hist,
                              uint8_t *__restrict__ rank8, uint32_t *lds_mask) {
+  constexpr int PER = (32 * MOE_ROUTE_MAX_TOPK + THREADS - 1) / THREADS;
   const int tid = threadIdx.x;
   __syncthreads();  // every wave done (lds_mask may share LDS with routing scratch)
-  for (int e = tid; e < e_out; e += BLOCK) lds_mask[e] = 0u;
+  for (int e = tid; e < e_out; e += THREADS) lds_mask[e] = 0u;
   __syncthreads();  // also orders this block's output stores before the reads below
   const int n = ntok * K;
   const int32_t *pk = packed + t_begin * K;
-  int ev[2], tv[2];
+  int ev[PER], tv[PER];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int i = tid + h * BLOCK;
+  for (int h = 0; h < PER; ++h) {
+    const int i = tid + h * THREADS;
     if (i < n) {
       ev[h] = pk[i] >> 16;
       tv[h] = i / K;
@@ -97,11 +100,11 @@ __device__ void block_counts(const int32_t *__restrict__ packed, int K, int e_ou
   }
   __syncthreads();
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int i = tid + h * BLOCK;
+  for (int h = 0; h < PER; ++h) {
+    const int i = tid + h * THREADS;
     if (i < n) rank8[t_begin * K + i] = (uint8_t)__popc(lds_mask[ev[h]] & ((1u << tv[h]) - 1u));
   }
-  for (int e = tid; e < e_out; e += BLOCK) hist[(size_t)e * nblk + blk] = __popc(lds_mask[e]);
+  for (int e = tid; e < e_out; e += THREADS) hist[(size_t)e * nblk + blk] = __popc(lds_mask[e]);
 }
 
 // ---------------------------------------------------------------------------
@@ -192,8 +195,8 @@ __global__ __launch_bounds__(BLOCK) void route_tokens_kernel(
     load_lane_layout<NP, LPG>(bias, p, lane, b);
     route_token<NP, LPG>(row, x, b, bias, p, lane, t, &lds.wave[wave], ids, wts, packed);
   }
-  block_counts(packed, p.K, p.e_out, tb, (int)min((int64_t)WAVES_PER_BLOCK, T - tb), blockIdx.x,
-               gridDim.x, pc.hist, pc.rank8, lds.mask);
+  block_counts<BLOCK>(packed, p.K, p.e_out, tb, (int)min((int64_t)WAVES_PER_BLOCK, T - tb),
+                     blockIdx.x, gridDim.x, pc.hist, pc.rank8, lds.mask);
 }
 
 // Prefill path, kernel 1 for the 896-expert, 8-group shape: four tokens per
@@ -201,10 +204,12 @@ __global__ __launch_bounds__(BLOCK) void route_tokens_kernel(
 // one token per wave. Then the block's share of the tile counts.
 __device__ unsigned long long g_row_fallback_tokens = 0ull;
 
-constexpr int ROWS_TOKENS_PER_BLOCK = 4 * WAVES_PER_BLOCK;
+constexpr int ROWS_WAVES = 4;
+constexpr int ROWS_BLOCK = 64 * ROWS_WAVES;
+constexpr int ROWS_TOKENS_PER_BLOCK = 4 * ROWS_WAVES;
 static_assert(ROWS_TOKENS_PER_BLOCK <= 32 && WAVES_PER_BLOCK <= 32, "32-bit token masks");
 
-__global__ __launch_bounds__(BLOCK, 8) void route_rows_kernel(
+__global__ __launch_bounds__(ROWS_BLOCK, 8) void route_rows_kernel(
     const float *__restrict__ logits, const float *__restrict__ bias, int T, RouteParams p,
     int32_t *__restrict__ ids, float *__restrict__ wts, int32_t *__restrict__ packed,
     PrefillCounts pc) {
@@ -214,11 +219,11 @@ __global__ __launch_bounds__(BLOCK, 8) void route_rows_kernel(
     union {
       rows::RowScratch r;
       WaveScratch w;
-    } wave[WAVES_PER_BLOCK];
+    } wave[ROWS_WAVES];
     uint32_t mask[MOE_ROUTE_MAX_EXPERTS];
   } lds;
   __shared__ int bad_bias;
-  const bool ok = rows::stage_bias<BLOCK>(bias, bias_lds, &bad_bias);  // all threads
+  const bool ok = rows::stage_bias<ROWS_BLOCK>(bias, bias_lds, &bad_bias);  // all threads
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int64_t tb = (int64_t)blockIdx.x * ROWS_TOKENS_PER_BLOCK;
@@ -243,8 +248,9 @@ __global__ __launch_bounds__(BLOCK, 8) void route_rows_kernel(
                         /*fast_first=*/false);
     }
   }
-  block_counts(packed, p.K, p.e_out, tb, (int)min((int64_t)ROWS_TOKENS_PER_BLOCK, T - tb),
-               blockIdx.x, gridDim.x, pc.hist, pc.rank8, lds.mask);
+  block_counts<ROWS_BLOCK>(packed, p.K, p.e_out, tb,
+                          (int)min((int64_t)ROWS_TOKENS_PER_BLOCK, T - tb), blockIdx.x,
+                          gridDim.x, pc.hist, pc.rank8, lds.mask);
 }
 
 // Prefill permutation, part 2: one block per output id: exclusive scan of
@@ -395,12 +401,10 @@ static hipError_t launch_route(const float *logits, const float *bias, int T, co
                                const moe_route_outputs *o, char *ws, hipStream_t st) {
   if (T <= MOE_ROUTE_MAX_FUSED_TOKENS) {
     const int grid = T > 0 ? (T + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK : 1;
-    if (g_ev_before) hipEventRecord(g_ev_before, st);
-    route_decode_kernel<NP, LPG><<<grid, BLOCK, 0, st>>>(logits, bias, T, rp, o->topk_ids,
-                                                     o->topk_weights, o->packed, o->counts,
-                                                     o->offsets, o->perm, o->inv_perm,
-                                                     reinterpret_cast<uint32_t *>(ws));
-    if (g_ev_after) hipEventRecord(g_ev_after, st);
+    hipExtLaunchKernelGGL(route_decode_kernel<NP, LPG>, dim3(grid), dim3(BLOCK), 0, st,
+                          g_ev_before, g_ev_after, 0, logits, bias, T, rp, o->topk_ids,
+                          o->topk_weights, o->packed, o->counts, o->offsets, o->perm,
+                          o->inv_perm, reinterpret_cast<uint32_t *>(ws));
     return hipGetLastError();
   }
   const bool rows_path = LPG == 8 && NP == 7 && rows_path_applies(rp, logits);
@@ -410,15 +414,16 @@ static hipError_t launch_route(const float *logits, const float *bias, int T, co
   pc.hist = reinterpret_cast<int32_t *>(ws + CONTROL_BYTES);
   pc.rank8 = reinterpret_cast<uint8_t *>(ws + CONTROL_BYTES +
                                          align256((size_t)nblk * rp.e_out * sizeof(int32_t)));
-  if (g_ev_before) hipEventRecord(g_ev_before, st);
+  // the benchmark hook's events are recorded by the launch itself
   if (rows_path) {
-    route_rows_kernel<<<nblk, BLOCK, 0, st>>>(logits, bias, T, rp, o->topk_ids, o->topk_weights,
-                                              o->packed, pc);
+    hipExtLaunchKernelGGL(route_rows_kernel, dim3(nblk), dim3(ROWS_BLOCK), 0, st, g_ev_before,
+                          g_ev_after, 0, logits, bias, T, rp, o->topk_ids, o->topk_weights,
+                          o->packed, pc);
   } else {
-    route_tokens_kernel<NP, LPG><<<nblk, BLOCK, 0, st>>>(logits, bias, T, rp, o->topk_ids,
-                                                     o->topk_weights, o->packed, pc);
+    hipExtLaunchKernelGGL(route_tokens_kernel<NP, LPG>, dim3(nblk), dim3(BLOCK), 0, st,
+                          g_ev_before, g_ev_after, 0, logits, bias, T, rp, o->topk_ids,
+                          o->topk_weights, o->packed, pc);
   }
-  if (g_ev_after) hipEventRecord(g_ev_after, st);
   block_prefix_kernel<<<rp.e_out, BLOCK, 0, st>>>(pc.hist, nblk, o->counts);
   const int64_t n = (int64_t)T * rp.K;
   const int64_t g3 = (n + BLOCK * SCATTER_PER_THREAD - 1) / (BLOCK * SCATTER_PER_THREAD);

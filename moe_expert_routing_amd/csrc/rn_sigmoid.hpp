@@ -200,4 +200,18 @@ __device__ __forceinline__ float sigmoid_rn32(float x) {
   return f;
 }
 
+// Two sigmoids at once: the two binary64 evaluations are independent, so
+// their latencies overlap (same results as sigmoid_rn32 on each input).
+__device__ __forceinline__ void sigmoid_rn32_x2(float x0, float x1, float &f0, float &f1) {
+  const float c0 = fminf(fmaxf(x0, SIG_ZERO_BELOW), SIG_ONE_ABOVE);
+  const float c1 = fminf(fmaxf(x1, SIG_ZERO_BELOW), SIG_ONE_ABOVE);
+  bool r0, r1;
+  f0 = rn32_checked(sigmoid_f64(c0), r0);
+  f1 = rn32_checked(sigmoid_f64(c1), r1);
+  if (r0) f0 = sigmoid_rn32_dd(c0);
+  if (r1) f1 = sigmoid_rn32_dd(c1);
+  f0 = x0 > SIG_ONE_ABOVE ? 1.0f : (x0 < SIG_ZERO_BELOW ? 0.0f : f0);
+  f1 = x1 > SIG_ONE_ABOVE ? 1.0f : (x1 < SIG_ZERO_BELOW ? 0.0f : f1);
+}
+
 }  // namespace moe

@@ -342,51 +342,62 @@ __device__ __forceinline__ void exact_top2(const float *__restrict__ row,
 }
 
 // Exact refinement of the rows with `need` set (call with the whole wave).
-// Exact group scores come from every
-// pool entry that can hold a group's top scores; then the exact top_k from
-// every kept-pool entry within twice the key error of the (top_k+1)-th
-// extracted key. Both steps decide on exact scores, so they only fail when
-// a pool is too short or the candidates exceed MAX_CAND. Returns true
-// (row-uniform) when the row has been written.
+// A row whose group choice the main path could not certify first gets exact
+// group scores, from every pool entry that can hold a group's top scores,
+// and a new extraction over the exactly kept groups; the other rows keep the
+// main path's kept groups and (top_k+1)-th key M. Then the exact top_k comes
+// from every kept-pool entry within twice the key error of M. Both steps
+// decide on exact scores, so they only fail when a pool is too short or the
+// candidates exceed MAX_CAND. Returns true (row-uniform) when the row has
+// been written.
 __device__ __forceinline__ bool refine_rows(const float *__restrict__ row,
                                             const float *__restrict__ bias_g,
                                             const uint32_t (&a)[PP], const uint32_t (&b)[PP],
-                                            bool need, const RouteParams &p, int r, int u,
-                                            int64_t t, RowScratch *L, int32_t *__restrict__ ids,
-                                            float *__restrict__ wts,
+                                            bool need, bool groups_ok, bool kept_a_in,
+                                            bool kept_b_in, uint32_t M_in, const RouteParams &p,
+                                            int r, int u, int64_t t, RowScratch *L,
+                                            int32_t *__restrict__ ids, float *__restrict__ wts,
                                             int32_t *__restrict__ packed) {
   const int K = p.K;
   const int c = u >> 2, sub = u & 3;
   if (need && u == 0) atomicAdd(&g_refined_tokens, 1ull);
-
-  // ---- exact group scores ------------------------------------------------------
-  // An expert whose key value is below thr is beaten, even exactly, by the
-  // two experts holding its group's approximate top-2 keys.
-  uint32_t a1 = a[0], a2 = a[1], b1 = b[0], b2 = b[1];
-  top2_merge(a1, a2, dpp<DPP_XOR1>(a1), dpp<DPP_XOR1>(a2));
-  top2_merge(a1, a2, dpp<DPP_XOR2>(a1), dpp<DPP_XOR2>(a2));
-  top2_merge(b1, b2, dpp<DPP_XOR1>(b1), dpp<DPP_XOR1>(b2));
-  top2_merge(b1, b2, dpp<DPP_XOR2>(b1), dpp<DPP_XOR2>(b2));
-  const double thra = (double)key_v(p.topn == 2 ? a2 : a1) - 2.0 * (double)row_err(key_v(a1));
-  const double thrb = (double)key_v(p.topn == 2 ? b2 : b1) - 2.0 * (double)row_err(key_v(b1));
-  const int na = need ? pool_count_ge(a, thra) : 0;
-  const int nb = need ? pool_count_ge(b, thrb) : 0;
-  bool fail = row_max((na >= PP || nb >= PP) ? 1u : 0u) != 0u;
-  uint32_t ta1, ta2, tb1, tb2;
-  exact_top2(row, bias_g, a, na, c, sub, ta1, ta2);
-  exact_top2(row, bias_g, b, nb, c, sub, tb1, tb2);
-  const float gxa = (p.topn == 2) ? ord_inv(ta1) + ord_inv(ta2) : ord_inv(ta1);
-  const float gxb = (p.topn == 2) ? ord_inv(tb1) + ord_inv(tb2) : ord_inv(tb1);
-  int ra, rb;
-  group_ranks(((uint64_t)ord_f32(gxa) << 3) | (uint64_t)(7 - c),
-              ((uint64_t)ord_f32(gxb) << 3) | (uint64_t)(3 - c), ra, rb);
-  const bool kept_a = ra < p.TG, kept_b = rb < p.TG;
-
-  // ---- extraction over the exactly kept groups ----------------------------------
-  uint32_t m[POOL];
-  merge_kept(a, b, kept_a, kept_b, m);
-  uint32_t rounds;
-  const uint32_t M = extract(m, K, rounds);
+  bool fail = false;
+  bool kept_a = kept_a_in, kept_b = kept_b_in;
+  uint32_t M = M_in;
+  const bool regroup = need && !groups_ok;
+  if (__ballot(regroup)) {
+    // ---- exact group scores ----------------------------------------------------
+    // An expert whose key value is below thr is beaten, even exactly, by the
+    // two experts holding its group's approximate top-2 keys.
+    uint32_t a1 = a[0], a2 = a[1], b1 = b[0], b2 = b[1];
+    top2_merge(a1, a2, dpp<DPP_XOR1>(a1), dpp<DPP_XOR1>(a2));
+    top2_merge(a1, a2, dpp<DPP_XOR2>(a1), dpp<DPP_XOR2>(a2));
+    top2_merge(b1, b2, dpp<DPP_XOR1>(b1), dpp<DPP_XOR1>(b2));
+    top2_merge(b1, b2, dpp<DPP_XOR2>(b1), dpp<DPP_XOR2>(b2));
+    const double thra = (double)key_v(p.topn == 2 ? a2 : a1) - 2.0 * (double)row_err(key_v(a1));
+    const double thrb = (double)key_v(p.topn == 2 ? b2 : b1) - 2.0 * (double)row_err(key_v(b1));
+    const int na = regroup ? pool_count_ge(a, thra) : 0;
+    const int nb = regroup ? pool_count_ge(b, thrb) : 0;
+    fail = row_max((na >= PP || nb >= PP) ? 1u : 0u) != 0u;
+    uint32_t ta1, ta2, tb1, tb2;
+    exact_top2(row, bias_g, a, na, c, sub, ta1, ta2);
+    exact_top2(row, bias_g, b, nb, c, sub, tb1, tb2);
+    const float gxa = (p.topn == 2) ? ord_inv(ta1) + ord_inv(ta2) : ord_inv(ta1);
+    const float gxb = (p.topn == 2) ? ord_inv(tb1) + ord_inv(tb2) : ord_inv(tb1);
+    int ra, rb;
+    group_ranks(((uint64_t)ord_f32(gxa) << 3) | (uint64_t)(7 - c),
+                ((uint64_t)ord_f32(gxb) << 3) | (uint64_t)(3 - c), ra, rb);
+    // ---- extraction over the exactly kept groups ------------------------------
+    uint32_t m[POOL];
+    merge_kept(a, b, ra < p.TG, rb < p.TG, m);
+    uint32_t rounds;
+    const uint32_t Mx = extract(m, K, rounds);
+    if (regroup) {
+      kept_a = ra < p.TG;
+      kept_b = rb < p.TG;
+      M = Mx;
+    }
+  }
 
   // ---- exact top_k from the candidates within the error band ----------------------
   const float vm = key_v(M);
@@ -411,35 +422,38 @@ __device__ __forceinline__ bool refine_rows(const float *__restrict__ row,
   }
   wave_lds_sync();
   const bool ok_m = need && !fail;
-  uint64_t ek[2] = {0ull, 0ull};
-  float es[2] = {0.0f, 0.0f};
-  int eid[2] = {0, 0};
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int j = u + LANES * h;
-    if (ok_m && j < mc) {
-      eid[h] = L->cand[r][j];
-      es[h] = sigmoid_rn32(row[eid[h]]);
-      const float sp = es[h] + bias_g[eid[h]];
-      ek[h] = ((uint64_t)ord_f32(sp) << 32) | (uint64_t)(~(uint32_t)eid[h]);
-      L->ekey[r][j] = ek[h];
-    }
-  }
+  // candidates u and u + 16 of the row, scored together
+  const bool v0 = ok_m && u < mc, v1 = ok_m && u + LANES < mc;
+  const int e0 = v0 ? L->cand[r][u] : 0, e1 = v1 ? L->cand[r][u + LANES] : 0;
+  float s0, s1;
+  sigmoid_rn32_x2(row[e0], row[e1], s0, s1);
+  const uint64_t k0 = v0 ? ((uint64_t)ord_f32(s0 + bias_g[e0]) << 32) | (uint64_t)(~(uint32_t)e0)
+                         : 0ull;
+  const uint64_t k1 = v1 ? ((uint64_t)ord_f32(s1 + bias_g[e1]) << 32) | (uint64_t)(~(uint32_t)e1)
+                         : 0ull;
+  if (v0) L->ekey[r][u] = k0;
+  if (v1) L->ekey[r][u + LANES] = k1;
   wave_lds_sync();
+  // ranks by counting: keys of the row, four per step (zero past mc)
   const int mmax = (int)wave_max_u32(ok_m ? (uint32_t)mc : 0u);
-  int rk[2] = {0, 0};
-  for (int j = 0; j < mmax; ++j) {
-    const uint64_t o = (ok_m && j < mc) ? L->ekey[r][j] : 0ull;
-    rk[0] += o > ek[0] ? 1 : 0;
-    rk[1] += o > ek[1] ? 1 : 0;
-  }
+  int rk0 = 0, rk1 = 0;
+  for (int j = 0; j < mmax; j += 4) {
+    uint64_t o[4];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int j = u + LANES * h;
-    if (ok_m && j < mc && rk[h] < K) {
-      L->slot[r][rk[h]] = make_uint2((uint32_t)eid[h], __float_as_uint(es[h]));
-      if (rk[h] == K - 1) L->kth[r] = ord_inv((uint32_t)(ek[h] >> 32));
+    for (int q = 0; q < 4; ++q) o[q] = (ok_m && j + q < mc) ? L->ekey[r][j + q] : 0ull;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      rk0 += o[q] > k0 ? 1 : 0;
+      rk1 += o[q] > k1 ? 1 : 0;
     }
+  }
+  if (v0 && rk0 < K) {
+    L->slot[r][rk0] = make_uint2((uint32_t)e0, __float_as_uint(s0));
+    if (rk0 == K - 1) L->kth[r] = ord_inv((uint32_t)(k0 >> 32));
+  }
+  if (v1 && rk1 < K) {
+    L->slot[r][rk1] = make_uint2((uint32_t)e1, __float_as_uint(s1));
+    if (rk1 == K - 1) L->kth[r] = ord_inv((uint32_t)(k1 >> 32));
   }
   wave_lds_sync();
   // every expert outside the candidates has key value < thb, so an exact
@@ -475,7 +489,8 @@ __device__ __forceinline__ uint32_t route_rows4(const float *__restrict__ logits
   uint32_t a[PP], b[PP];
   stream_pools(row, bias_lds, c, sub, a, b);
   bool kept_a, kept_b;
-  bool fail = !approx_groups(a, b, p, c, kept_a, kept_b);
+  const bool groups_ok = approx_groups(a, b, p, c, kept_a, kept_b);  // row-uniform
+  bool fail = !groups_ok;
   uint32_t m[POOL];
   merge_kept(a, b, kept_a, kept_b, m);
   uint32_t rounds;
@@ -543,7 +558,9 @@ __device__ __forceinline__ uint32_t route_rows4(const float *__restrict__ logits
   const bool need = !done && valid;
   if (__ballot(need)) {
     wave_lds_sync();
-    done = refine_rows(row, bias_g, a, b, need, p, r, u, t, L, ids, wts, packed) || done;
+    done = refine_rows(row, bias_g, a, b, need, groups_ok, kept_a, kept_b, M, p, r, u, t, L, ids,
+                       wts, packed) ||
+           done;
   }
   // rows to route again
   const uint64_t fb = __ballot(!done && valid && u == 0);
