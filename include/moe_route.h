@@ -199,7 +199,10 @@ int64_t moe_route_exact_path_tokens(int32_t reset);
  *           (896 experts, 8 groups, top_k <= 16, more than 64 tokens), taken
  *           when its fast certificate does not hold;
  *   path 2: tokens of that path routed again one token per wave because the
- *           refinement could not decide either.
+ *           refinement could not decide either;
+ *   path 3: tokens of the one-token-per-wave fast path whose candidates were
+ *           scored again exactly because the certificate on approximate
+ *           candidate scores did not hold (near-ties among the candidates).
  * reset != 0 zeroes that path's count. Returns the count, MOE_ERR_UNSUPPORTED
  * for another path, or MOE_ERR_HIP.
  */

@@ -258,12 +258,13 @@ def exact_path_tokens(reset: bool = False) -> int:
     return int(v)
 
 
-PATH_EXACT, PATH_REFINED, PATH_REROUTED = 0, 1, 2
+PATH_EXACT, PATH_REFINED, PATH_REROUTED, PATH_RESCORED = 0, 1, 2, 3
 
 
 def path_tokens(path: int, reset: bool = False) -> int:
     """Diagnostic: tokens that took a kernel path since the last reset
-    (PATH_EXACT, PATH_REFINED or PATH_REROUTED; see moe_route_path_tokens)."""
+    (PATH_EXACT, PATH_REFINED, PATH_REROUTED or PATH_RESCORED; see
+    moe_route_path_tokens)."""
     v = lib().moe_route_path_tokens(path, 1 if reset else 0)
     if v < 0:
         _check(int(v), "moe_route_path_tokens")

@@ -35,6 +35,20 @@ namespace moe {
 constexpr int WAVES_PER_BLOCK = 4;
 constexpr int BLOCK = 64 * WAVES_PER_BLOCK;
 constexpr size_t CONTROL_BYTES = 256;
+// Inclusive prefix sum over the 64 lanes: shifts by 1, 2, 4, 8 within each
+// row of 16 lanes, then row 0's total into row 1 and row 2's into row 3
+// (row_bcast:15), then rows 0-1's total into rows 2-3 (row_bcast:31).
+// A lane with no source, or in a row the mask leaves out, adds 0.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return v;
+}
+
 // Exclusive scan of in[0..n) (n <= 1024, any memory) into out[0..n] in LDS,
 // out[n] = total. All BLOCK threads must call it.
 __device__ void block_exclusive_scan(const int32_t *in, int n, int32_t *out, int32_t *wave_tot) {
@@ -48,12 +62,7 @@ __device__ void block_exclusive_scan(const int32_t *in, int n, int32_t *out, int
     v[k] = idx < n ? in[idx] : 0;
     s += v[k];
   }
-  int incl = s;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(incl, d);
-    if (lane >= d) incl += o;
-  }
+  const int incl = wave_inclusive_scan(s);
   if (lane == 63) wave_tot[wv] = incl;
   __syncthreads();
   int wave_off = 0;
@@ -139,13 +148,31 @@ __global__ __launch_bounds__(BLOCK) void route_decode_kernel(
   if (!is_last) return;
   __threadfence();
 
+  // Every entry's output id, read once: PER loads per thread issued back to
+  // back (indices past the end read the last entry and are not used).
+  constexpr int PER = (MOE_ROUTE_MAX_FUSED_TOKENS * MOE_ROUTE_MAX_TOPK + BLOCK - 1) / BLOCK;
+  static_assert(MOE_ROUTE_MAX_FUSED_TOKENS * MOE_ROUTE_MAX_TOPK <= 2048, "entry range");
   const int n = T * p.K;
-  for (int i = threadIdx.x; i < p.e_out; i += BLOCK) mask[i] = 0ull;
-  __syncthreads();
-  for (int f = threadIdx.x; f < n; f += BLOCK) {
-    const int e = packed[f] >> 16;
-    atomicOr(&mask[e], 1ull << (f / p.K));
+  // token of entry f = f / K as a multiply-high (exact for f < 2048, K <= 32)
+  const uint32_t kinv = 0xFFFFFFFFu / (uint32_t)p.K + 1u;
+  int ev[PER], tv[PER];
+#pragma unroll
+  for (int h = 0; h < PER; ++h) ev[h] = 0;
+  if (n > 0) {
+#pragma unroll
+    for (int h = 0; h < PER; ++h) ev[h] = packed[min((int)threadIdx.x + h * BLOCK, n - 1)];
   }
+  for (int i = threadIdx.x; i < p.e_out; i += BLOCK) mask[i] = 0ull;
+#pragma unroll
+  for (int h = 0; h < PER; ++h) {
+    const int f = min((int)threadIdx.x + h * BLOCK, max(n - 1, 0));
+    ev[h] >>= 16;
+    tv[h] = p.K == 1 ? f : (int)__umulhi((uint32_t)f, kinv);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < PER; ++h)
+    if ((int)threadIdx.x + h * BLOCK < n) atomicOr(&mask[ev[h]], 1ull << tv[h]);
   __syncthreads();
   for (int i = threadIdx.x; i < p.e_out; i += BLOCK) {
     const int c = __popcll(mask[i]);
@@ -155,12 +182,16 @@ __global__ __launch_bounds__(BLOCK) void route_decode_kernel(
   __syncthreads();
   block_exclusive_scan(offs, p.e_out, offs, wave_tot);  // in place: reads precede writes
   for (int i = threadIdx.x; i <= p.e_out; i += BLOCK) offsets[i] = offs[i];
-  for (int f = threadIdx.x; f < n; f += BLOCK) {
-    const int e = packed[f] >> 16;
-    const int tok = f / p.K;
-    const int pos = offs[e] + __popcll(mask[e] & ((1ull << tok) - 1ull));
-    perm[pos] = f;
-    if (inv) inv[f] = pos;
+  // LDS reads for every slot (clamped entries are valid ids), stores for
+  // the real entries
+#pragma unroll
+  for (int h = 0; h < PER; ++h) {
+    const int f = threadIdx.x + h * BLOCK;
+    const int pos = offs[ev[h]] + __popcll(mask[ev[h]] & ((1ull << tv[h]) - 1ull));
+    if (f < n) {
+      perm[pos] = f;
+      if (inv) inv[f] = pos;
+    }
   }
   if (threadIdx.x == 0) *ticket = 0u;  // leave the control block zeroed
 }
@@ -273,12 +304,7 @@ __global__ __launch_bounds__(BLOCK) void block_prefix_kernel(int32_t *__restrict
       v[k] = (beg + k < nblk) ? row[beg + k] : 0;
       sum += v[k];
     }
-    int incl = sum;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int o = __shfl_up(incl, d);
-      if (lane >= d) incl += o;
-    }
+    const int incl = wave_inclusive_scan(sum);
     if (lane == 63) wave_tot[wv] = incl;
     __syncthreads();
     int off = carry, total = 0;
@@ -566,6 +592,7 @@ int64_t moe_route_path_tokens(int32_t path, int32_t reset) {
     case 0: return moe_route_exact_path_tokens(reset);
     case 1: sym = &moe::rows::g_refined_tokens; break;
     case 2: sym = &moe::g_row_fallback_tokens; break;
+    case 3: sym = &moe::g_rescored_tokens; break;
     default: return MOE_ERR_UNSUPPORTED;
   }
   unsigned long long v = 0ull;

@@ -19,11 +19,14 @@
 //     turned into a 32-bit key (value bits with the slot in the low 4 bits).
 //  2. The group choice is accepted only when the score margin between the
 //     kept and the dropped groups exceeds the error bound.
-//  3. A threshold, found by bisection on the kept lanes' top-2 keys, picks
+//  3. A threshold, found by bisection on the kept lanes' top-5 keys, picks
 //     a candidate set (<= 64) holding every possible winner; the candidates
-//     are scored EXACTLY and ranked by exact (sp, id).
-//  4. The result is accepted only when the exact top_k-th score beats the
-//     largest score any non-candidate can have.
+//     are scored again (same approximation) and ranked by (sp~, id).
+//  4. The result is accepted only when the top_k-th score beats the largest
+//     score any non-candidate can have and adjacent ranks are apart by more
+//     than the error (or are exact twins). Otherwise the candidates are
+//     scored EXACTLY and ranked by exact (sp, id), and the result is accepted
+//     when the exact top_k-th score beats that bound.
 // A token that fails a check runs the same pipeline on exact scores (only
 // the key truncation is left to bound), and if that cannot decide either
 // (near-ties within 16 ulp at the threshold), route_token_exact: exact
@@ -62,6 +65,8 @@ struct RouteParams {
 
 // Tokens that took the exact path (diagnostic, moe_route_exact_path_tokens).
 __device__ unsigned long long g_exact_path_tokens = 0ull;
+// Tokens of the fast path whose candidates were scored again exactly.
+__device__ unsigned long long g_rescored_tokens = 0ull;
 
 // Lanes per group: a compile-time constant (LPG > 0) or the runtime value
 // (LPG = 0). The common shapes get constant loops and lane indices.
@@ -200,9 +205,12 @@ __device__ __forceinline__ float key_value(uint32_t k) { return __uint_as_float(
 // whose key is not clamped: the approximation error, two binary32 roundings
 // (of s~ + b and of s + b) and the 15-ulp truncation, with margin.
 __device__ __forceinline__ float err_bound(float v) { return 1.01f * FAST_SIG_ERR + 0x1p-18f * v; }
-// Same for a group score of up to two terms plus its own rounding.
+// Same for a group score v = fl32(v1 + v2): per term the truncation
+// (< 15/16 * 2^-19 * v_i) and the two roundings (2^-23 * v_i), plus the
+// roundings of the approximate and the exact sum (2^-23 * v), stay below
+// 2 * FAST_SIG_ERR + 17/16 * 2^-19 * v; 2^-18 * v leaves a margin.
 __device__ __forceinline__ float group_err_bound(float v) {
-  return 2.02f * FAST_SIG_ERR + 0x1p-17f * v;
+  return 2.02f * FAST_SIG_ERR + 0x1p-18f * v;
 }
 
 template <int NP, int LPG>
@@ -250,6 +258,76 @@ __device__ __forceinline__ float score_err(float v) {
   return 1.01f * FAST_SIG_ERR + 0x1p-22f * fabsf(v);
 }
 
+// Exact group choice for a token whose approximate group scores leave the
+// kept/dropped boundary within the error. A group's exact top-`topn` scores
+// are among its experts whose approximate key value reaches
+// thr = (approximate topn-th value) - 2 * err_bound(approximate top value):
+// every expert below thr scores, exactly, below the exact scores of the
+// group's approximate top-topn. Each lane holds its 5 best keys; when its
+// 5th reaches thr the pool may not hold every such expert and the function
+// returns false. Otherwise those pool entries (at most 4 per lane; logits
+// and biases read again, from cache) are scored exactly, each group's exact score is the fl32 sum of its exact top
+// `topn`, and kept = the TG best groups (ties -> lower group index).
+__device__ __forceinline__ bool exact_group_choice(const float *__restrict__ row,
+                                                   const float *__restrict__ bias_g, uint32_t p1,
+                                                   uint32_t p2, uint32_t p3, uint32_t p4,
+                                                   uint32_t p5, uint32_t g1, uint32_t g2,
+                                                   const RouteParams &p, int lane, int e0, int lpg,
+                                                   int lpg_log2, int G, bool &kept) {
+  const float thr = key_value(p.topn == 2 ? g2 : g1) - 2.0f * err_bound(key_value(g1));
+  if (__ballot(key_value(p5) >= thr)) return false;
+  const uint32_t pool[4] = {p1, p2, p3, p4};
+  uint32_t e1 = 0u, e2 = 0u;  // the lane's exact top-2 (ord_f32; 0 = none)
+#pragma unroll
+  for (int i = 0; i < 4; i += 2) {
+    const bool u0 = key_value(pool[i]) >= thr, u1 = key_value(pool[i + 1]) >= thr;
+    if (!__ballot(u0 || u1)) break;  // pools are sorted: later entries are lower
+    // thr > 0 here, so a selected entry is a filled pool entry: valid slot
+    const int d0 = slot_expert(e0, lpg, 15 - (int)(pool[i] & 15u));
+    const int d1 = slot_expert(e0, lpg, 15 - (int)(pool[i + 1] & 15u));
+    const float x0 = u0 ? row[d0] : 0.0f, b0 = u0 ? bias_g[d0] : 0.0f;
+    const float x1 = u1 ? row[d1] : 0.0f, b1 = u1 ? bias_g[d1] : 0.0f;
+    const float s0 = sigmoid_rn32(x0), s1 = sigmoid_rn32(x1);
+    const uint32_t k0 = u0 ? ord_f32(s0 + b0) : 0u;
+    const uint32_t k1 = u1 ? ord_f32(s1 + b1) : 0u;
+    top2_merge(e1, e2, umax(k0, k1), umin(k0, k1));
+  }
+  group_top2(e1, e2, lpg);
+  auto val = [](uint32_t k) {  // inverse of ord_f32 (k != 0)
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+  };
+  const float gs = (p.topn == 2) ? val(e1) + val(e2) : val(e1);
+  const int g = lane >> lpg_log2;
+  int rank = 0;
+  for (int gg = 0; gg < G; ++gg) {
+    const float o = __uint_as_float(readlane_u32(__float_as_uint(gs), gg << lpg_log2));
+    rank += ((o > gs) || (o == gs && gg < g)) ? 1 : 0;
+  }
+  kept = rank < p.TG;
+  return true;
+}
+
+// Ranks the m candidates (lanes 0..m-1 hold expert eid, logit cx, bias cb
+// and score sc) by (score desc, id asc) and stores ranks 0..K in L->res.
+__device__ __forceinline__ void rank_candidates(WaveScratch *L, int lane, int m, int K,
+                                                uint32_t eid, float cx, float cb, float sc) {
+  const bool is_cand = lane < m;
+  const uint64_t ck = ((uint64_t)ord_f32(sc) << 32) | (uint64_t)(~eid);
+  if (is_cand) L->key[lane] = ck;
+  if (lane >= m && lane < ((m + 3) & ~3)) L->key[lane] = 0ull;  // pad to a multiple of 4
+  wave_lds_sync();
+  int r = 0;
+  if (is_cand) {
+    for (int j = 0; j < m; j += 4) {
+      const uint64_t k0 = L->key[j], k1 = L->key[j + 1], k2 = L->key[j + 2], k3 = L->key[j + 3];
+      r += (k0 > ck ? 1 : 0) + (k1 > ck ? 1 : 0) + (k2 > ck ? 1 : 0) + (k3 > ck ? 1 : 0);
+    }
+  }
+  if (is_cand && r <= K)
+    L->res[r] = make_uint4(eid, __float_as_uint(cx), __float_as_uint(cb), __float_as_uint(sc));
+  wave_lds_sync();
+}
+
 // Selects the top_k experts of one token. The scores that pick the groups
 // and the candidates are the fast approximations (EXACT = false) or the
 // exact scores (EXACT = true). Returns true, with (id, exact s) of slot
@@ -266,7 +344,9 @@ __device__ __forceinline__ bool select_token(const float *__restrict__ row,
   const int g = lane >> lpg_log2;
   const int e0 = g * (LPG ? M * LPG : p.eg) + 2 * (lane & (lpg - 1));
 
-  // ---- streaming: scores -> keys -> the lane's top-4 keys ------------------
+  bool rescored = false;  // some scores were recomputed exactly (fast path)
+
+  // ---- streaming: scores -> keys -> the lane's top-5 keys ------------------
   uint32_t p1 = 0u, p2 = 0u, p3 = 0u, p4 = 0u, p5 = 0u;
   float x1 = -__builtin_inff(), x2 = -__builtin_inff();  // exact top-2 (EXACT)
 #pragma unroll
@@ -314,16 +394,26 @@ __device__ __forceinline__ bool select_token(const float *__restrict__ row,
       if (i == p.TG - 1) keep_thr = srt[i];
       if (i == p.TG) drop_max = srt[i];
     }
+    bool near_tie = false;
     if (p.TG < G) {
       const float kmin = __uint_as_float(keep_thr), dmax = __uint_as_float(drop_max);
-      if (!(kmin - group_err_bound(kmin) > dmax + group_err_bound(dmax))) return false;
+      near_tie = !(kmin - group_err_bound(kmin) > dmax + group_err_bound(dmax));
     }
-    hi_key = 0u;
+    if (!near_tie) {
+      hi_key = 0u;
 #pragma unroll
-    for (int gg = 0; gg < 8; ++gg)
-      if (gg < G && sv[gg] >= keep_thr) hi_key = umax(hi_key, top[gg]);
-    hi_key += 1u;
-    kept = __float_as_uint(gs) >= keep_thr;
+      for (int gg = 0; gg < 8; ++gg)
+        if (gg < G && sv[gg] >= keep_thr) hi_key = umax(hi_key, top[gg]);
+      hi_key += 1u;
+      kept = __float_as_uint(gs) >= keep_thr;
+    } else {
+      // Kept and dropped groups within the error: exact group scores.
+      if (!exact_group_choice(row, bias_g, p1, p2, p3, p4, p5, g1, g2, p, lane, e0, lpg, lpg_log2,
+                              G, kept))
+        return false;
+      rescored = true;
+      hi_key = wave_max_u32(kept ? p1 : 0u) + 1u;
+    }
     // the kept groups' scores must rest on unclamped (positive) values
     if (__ballot(kept && (glast & 0xFFFFFFF0u) == 0u)) return false;
   } else {
@@ -425,28 +515,14 @@ __device__ __forceinline__ bool select_token(const float *__restrict__ row,
   // ---- candidates: scores and ranks by (score desc, id asc) ---------------
   const bool is_cand = lane < m;
   uint32_t eid = 0u;
-  float cx = 0.0f, cb = 0.0f, csc = 0.0f;
-  uint64_t ck = 0ull;
+  float cx = 0.0f, cb = 0.0f;
   if (is_cand) {
     eid = L->cand[lane];
     cx = row[eid];
     cb = bias_g[eid];
-    csc = (EXACT ? sigmoid_rn32(cx) : fast_sigmoid(cx)) + cb;
-    ck = ((uint64_t)ord_f32(csc) << 32) | (uint64_t)(~eid);
-    L->key[lane] = ck;
   }
-  if (lane >= m && lane < ((m + 3) & ~3)) L->key[lane] = 0ull;  // pad to a multiple of 4
-  wave_lds_sync();
-  int r = 0;
-  if (is_cand) {
-    for (int j = 0; j < m; j += 4) {
-      const uint64_t k0 = L->key[j], k1 = L->key[j + 1], k2 = L->key[j + 2], k3 = L->key[j + 3];
-      r += (k0 > ck ? 1 : 0) + (k1 > ck ? 1 : 0) + (k2 > ck ? 1 : 0) + (k3 > ck ? 1 : 0);
-    }
-  }
-  if (is_cand && r <= p.K)
-    L->res[r] = make_uint4(eid, __float_as_uint(cx), __float_as_uint(cb), __float_as_uint(csc));
-  wave_lds_sync();
+  rank_candidates(L, lane, m, p.K, eid, cx, cb,
+                  (EXACT ? sigmoid_rn32(cx) : fast_sigmoid(cx)) + cb);
 
   // ---- certificate -----------------------------------------------------------
   // slot k = lane for lanes 0..K-1; rank K is the best non-winner
@@ -458,19 +534,32 @@ __device__ __forceinline__ bool select_token(const float *__restrict__ row,
   }
   // the K-th score must beat every non-candidate (keys below theta)
   const float tau = key_value(theta);
-  const float kth = __uint_as_float(readlane_u32(rr.w, p.K - 1));
+  float kth = __uint_as_float(readlane_u32(rr.w, p.K - 1));
   if (EXACT) {
     if (!(kth > tau + 0x1p-19f * tau)) return false;
   } else {
-    if (!(kth - score_err(kth) > tau + score_err(tau) + 0x1p-19f * tau)) return false;
-    // adjacent winners (and the K-th vs the best non-winner) must be apart
-    // by more than the error, or be exact twins (same logit and bias)
-    const bool check = lane < p.K && (lane < p.K - 1 || has_next);
-    const float rv = __uint_as_float(rr.w), nv = __uint_as_float(nr.w);
-    const bool sep = (rv - score_err(rv)) > (nv + score_err(nv));
-    const bool twin = (rr.y == nr.y) && (rr.z == nr.z);
-    if (__ballot(check && !(sep || twin))) return false;
+    bool ok = kth - score_err(kth) > tau + score_err(tau) + 0x1p-19f * tau;
+    if (ok) {
+      // adjacent winners (and the K-th vs the best non-winner) must be apart
+      // by more than the error, or be exact twins (same logit and bias)
+      const bool check = lane < p.K && (lane < p.K - 1 || has_next);
+      const float rv = __uint_as_float(rr.w), nv = __uint_as_float(nr.w);
+      const bool sep = (rv - score_err(rv)) > (nv + score_err(nv));
+      const bool twin = (rr.y == nr.y) && (rr.z == nr.z);
+      ok = !__ballot(check && !(sep || twin));
+    }
+    if (!ok) {
+      // Near-ties among the candidates: score them exactly and rank again.
+      // The candidate set still holds every possible winner when the exact
+      // K-th score beats the largest exact score a non-candidate can have.
+      rescored = true;
+      rank_candidates(L, lane, m, p.K, eid, cx, cb, sigmoid_rn32(cx) + cb);
+      if (lane < p.K) rr = L->res[lane];
+      kth = __uint_as_float(readlane_u32(rr.w, p.K - 1));
+      if (!(kth > tau + score_err(tau) + 0x1p-19f * tau)) return false;
+    }
   }
+  if (!EXACT && rescored && lane == 0) atomicAdd(&g_rescored_tokens, 1ull);
   // the weights use the exact s of the winners
   const float wx = __uint_as_float(rr.y);
   my_id = (int)rr.x;

@@ -306,6 +306,23 @@ def _near_tie_case(T=256, seed=9):
     return W.RouteCase("near_ties", logits, bias, off=224, cnt=112)
 
 
+def test_decode_rescores_near_ties():
+    """Decode tokens whose best non-winner sits within a few ulp of the 16th
+    winner (odd rows) fail the certificate on approximate candidate scores,
+    and their candidates are scored again exactly; tokens whose 5th group
+    sits within a few ulp of the 4th (even rows) get exact group scores from
+    their pools. Both give the oracle's answer."""
+    c = _near_tie_case(T=64, seed=11)
+    for path in (M.PATH_EXACT, M.PATH_RESCORED):
+        M.path_tokens(path, reset=True)
+    say("case near ties T=64 (decode)")
+    assert_parity(run_case(c), oracle_case(c), c.name)
+    rescored = M.path_tokens(M.PATH_RESCORED, reset=True)
+    exact = M.path_tokens(M.PATH_EXACT, reset=True)
+    say(f"rescored {rescored}, exact pipeline {exact}")
+    assert rescored >= 48, (rescored, exact)
+
+
 def test_prefill_rows_refine_near_ties():
     c = _near_tie_case()
     for path in (M.PATH_EXACT, M.PATH_REFINED, M.PATH_REROUTED):
