@@ -34,7 +34,10 @@ HBM_PEAK_GBPS = 8000.0
 BYTES_PER_TOKEN_PATH = 3904     # logits 3584 + ids, weights, packed, perm, inv (5 x 64)
 BYTES_PER_TOKEN_ROUTE_KERNEL = 3776  # logits 3584 + ids, weights, packed (3 x 64)
 COPY_BYTES = 512 << 20
-PROFILE_PMC = os.path.join(ROOT, "profiles", "pmc_route_tokens_long_prefill_32768.txt")
+PROFILE_PMC = os.path.join(ROOT, "profiles", "pmc_route_rows_long_prefill_32768.txt")
+# sources the routing kernels are built from (the router GEMM is not among them)
+ROUTE_SOURCES = ("internal.hpp", "moe_route.hip", "rn_sigmoid.hpp", "route_rows.hpp",
+                 "route_wave.hpp")
 
 
 def log(msg: str) -> None:
@@ -55,7 +58,7 @@ def parse():
 def source_digest() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "moe_expert_routing_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in ROUTE_SOURCES:
         with open(os.path.join(csrc, name), "rb") as fh:
             h.update(name.encode() + fh.read())
     return h.hexdigest()[:16]

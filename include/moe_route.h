@@ -150,7 +150,11 @@ size_t moe_router_gemm_route_workspace_bytes(int32_t num_tokens, int32_t hidden,
  * memory table: router 0.59 B parameters).
  *   hidden_bf16 [T, H] bf16 bit patterns, weight_bf16 [E, H] bf16 bit
  *   patterns, H a multiple of 64; logits_out [T, E] fp32 (required: the
- *   routing reads the logits from it).
+ *   routing reads the logits from it). hidden_bf16, weight_bf16 and
+ *   logits_out must be 16-byte aligned (else MOE_ERR_SHAPE), the workspace
+ *   too (else MOE_ERR_WORKSPACE). The accumulation order along H depends on
+ *   the token count (K is split when the tiles do not fill the device), not
+ *   on timing: the same inputs give the same logits on every call.
  */
 int moe_router_gemm_route(const uint16_t *hidden_bf16,
                           const uint16_t *weight_bf16, int32_t num_tokens,

@@ -7,13 +7,26 @@
 // operands keep the hidden dimension contiguous, so each lane's MFMA operand
 // is one 16-byte run of 8 bf16 along K.
 //
-// Tiling: a block of 4 waves computes a 64 (tokens) x 64 (experts) tile;
-// each wave owns 32 x 32 = 2 x 2 tiles of v_mfma_f32_16x16x32_bf16. K is
-// staged through LDS in steps of 64. When there are too few tiles to fill the
-// chip (decode), K is split into S equal ranges; each writes its own fp32
-// partial and a second kernel sums the S partials in a fixed order, so the
-// result does not depend on timing. Logits are written, never accumulated
-// into existing memory.
+// Kernel. A block of 4 waves computes a TM (tokens) x TN (experts) tile on
+// the matrix cores; each wave owns a WM x WN sub-tile. K advances in stages
+// of 64: each stage's A and B tiles go from global memory straight into LDS
+// (global_load_lds_dwordx4, no register staging), NS stage buffers deep, so
+// NS - 1 stages are in flight while one is consumed; the next stage's
+// operand fragments are read from LDS while the current stage's MFMAs run.
+// An LDS row holds 64 bf16 = 8 chunks of 16 bytes; chunk c of row r sits at
+// position c ^ (r & 7), which makes every 8-lane group of a fragment read
+// (8 rows, one chunk) hit 8 different bank quads.
+//
+// Shapes (v_mfma_f32_16x16x32_bf16, 4 stage buffers). Decode (T <= 128),
+// bound by reading W once: 64 x 64 tiles, 32 x 32 per wave. Prefill:
+// 128 x 128 tiles, 64 x 64 per wave. (Measured on MI355X: 32x32x16 MFMA
+// tiles and deeper stage rings were both slower here.) When
+// the tiles do not fill the chip, K is split into S equal ranges; each
+// writes its own fp32 partial and a second kernel sums the S partials in a
+// fixed order, so the result does not depend on timing. Blocks are numbered
+// so that the blocks the hardware places on one XCD (every 8th block) share
+// operand rows in that XCD's L2. Logits are written, never accumulated into
+// existing memory.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -24,119 +37,268 @@ namespace moe_gemm {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+typedef __attribute__((address_space(1))) void *gbl_ptr_t;
 
-constexpr int BM = 64, BN = 64, BK = 64;
-constexpr int THREADS = 256;
-constexpr int LDS_STRIDE = BK + 8;  // bf16 elements per LDS row (16-byte pad)
+constexpr int TK = 64;          // K per stage (bf16): one 128-byte LDS row
+constexpr int THREADS = 256;    // 4 waves
 constexpr int MAX_SPLITS = 16;
+constexpr int DECODE_MAX_T = 128;
 
-// Pick the K split: the largest divisor of H/BK not above the count that
-// brings the grid to about 512 blocks (at most MAX_SPLITS).
-static int pick_splits(int T, int E, int H) {
-  const int mt = (T + BM - 1) / BM, nt = E / BN;
-  const int tiles = mt * nt;
-  int want = (512 + tiles - 1) / tiles;
-  if (want > MAX_SPLITS) want = MAX_SPLITS;
-  const int kb = H / BK;
-  int s = 1;
-  for (int d = 1; d <= want; ++d)
-    if (kb % d == 0) s = d;
-  return s;
+template <int TM_, int TN_, int WM_, int WN_, int MF_, int NS_>
+struct Tile {
+  static constexpr int TM = TM_, TN = TN_, WM = WM_, WN = WN_;
+  static constexpr int MF = MF_;    // MFMA tile: 16 (16x16x32) or 32 (32x32x16)
+  static constexpr int NS = NS_;    // LDS stage buffers
+  static constexpr int KMF = MF == 16 ? 32 : 16;  // K per MFMA
+  static constexpr int KSTEPS = TK / KMF;
+  static constexpr int WAVES_N = TN / WN;
+  static_assert((TM / WM) * (TN / WN) == 4, "four waves");
+  static_assert(WM % MF == 0 && WN % MF == 0, "whole MFMA tiles");
+  static constexpr int FM = WM / MF, FN = WN / MF;  // MFMA tiles per wave
+  static constexpr int A_BYTES = TM * TK * 2, B_BYTES = TN * TK * 2;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  // one load instruction fills 8 LDS rows (64 lanes x 16 bytes)
+  static constexpr int A_LOADS = TM / 32, B_LOADS = TN / 32;  // per wave per stage
+  static constexpr int LOADS = A_LOADS + B_LOADS;
+  static_assert((NS - 2) * LOADS <= 63, "vmcnt range");
+};
+using DecodeTile = Tile<64, 64, 32, 32, 16, 4>;
+using PrefillTile = Tile<128, 128, 64, 64, 16, 4>;
+
+template <int MF>
+struct MfmaAcc;
+template <>
+struct MfmaAcc<16> {
+  typedef f32x4 type;
+};
+template <>
+struct MfmaAcc<32> {
+  typedef f32x16 type;
+};
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__global__ __launch_bounds__(THREADS) void router_gemm_kernel(
-    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, float *__restrict__ C,
-    int T, int E, int H, int k_per_split) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDS_STRIDE];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int n0 = blockIdx.x * BN;
-  const int m0 = blockIdx.y * BM;
-  const int split = blockIdx.z;
-  const int kbeg = split * k_per_split;
-  float *Cs = C + (size_t)split * T * E;
+// s_waitcnt vmcnt(n) for a run-time n in [0, MAXN] with the count encoded as
+// an immediate.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_imm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+template <int STEP, int MAXK>
+__device__ __forceinline__ void wait_vmcnt_steps(int k) {
+  if constexpr (MAXK > 0) {
+    if (k >= MAXK) {
+      wait_vmcnt_imm<MAXK * STEP>();
+      return;
+    }
+    wait_vmcnt_steps<STEP, MAXK - 1>(k);
+  } else {
+    wait_vmcnt_imm<0>();
+  }
+}
 
-  // global -> LDS: 64 rows x 128 bytes per operand = 512 16-byte pieces,
-  // two per thread.
-  const int lr = tid >> 3;         // 0..31
-  const int lc = (tid & 7) * 8;    // bf16 column of the 16-byte piece
-  const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
-  const int fr = lane & 15, fk = (lane >> 4) * 8;
+// Workgroup barrier that orders LDS accesses for the compiler without
+// waiting for the stage loads still in flight (a __syncthreads() would wait
+// for every outstanding load). Each wave first waits for its own LDS reads,
+// so that no fragment read of a buffer is still pending when another wave's
+// loads start refilling it.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
-  f32x4 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+// Tile index of this block: the hardware sends block b to XCD b % 8, so the
+// blocks of one XCD take a contiguous run of tiles (same token rows, every
+// expert tile) when the tile count is a multiple of 8.
+__device__ __forceinline__ int tile_of_block(int b, int ntiles) {
+  if (ntiles % 8 != 0) return b;
+  return (b % 8) * (ntiles / 8) + b / 8;
+}
 
-  uint4 ra[2], rb[2];
-  auto gload = [&](int k0) {
+template <class C>
+__global__ __launch_bounds__(THREADS, 1) void router_gemm_kernel(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, float *__restrict__ Cout,
+    int T, int E, int H, int k_per_split, int m_tiles, int n_tiles) {
+  typedef typename MfmaAcc<C::MF>::type Acc;
+  constexpr int NS = C::NS, MF = C::MF;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * C::STAGE_BYTES];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tile = tile_of_block(blockIdx.x, (int)gridDim.x);
+  const int split = tile / (m_tiles * n_tiles);
+  const int mt = (tile / n_tiles) % m_tiles, nt = tile % n_tiles;
+  const int m0 = mt * C::TM, n0 = nt * C::TN, kbeg = split * k_per_split;
+  const int nk = k_per_split / TK;
+  float *Cs = Cout + (size_t)split * T * E;
+
+  // Load q of this wave fills LDS rows R..R+7, R = (wave * LOADS_X + q) * 8;
+  // lane i writes row R + i/8 at position i%8, which holds global chunk
+  // (i%8) ^ (i/8). Rows past the last token read the last token's row.
+  const int lr = lane >> 3, lchunk = (lane & 7) ^ lr;
+  const uint16_t *a_src[C::A_LOADS];
+  const uint16_t *b_src[C::B_LOADS];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int r = lr + 32 * h;
-      const int tm = m0 + r;
-      ra[h] = tm < T ? *reinterpret_cast<const uint4 *>(A + (size_t)tm * H + k0 + lc)
-                     : make_uint4(0u, 0u, 0u, 0u);
-      rb[h] = *reinterpret_cast<const uint4 *>(B + (size_t)(n0 + r) * H + k0 + lc);
+  for (int q = 0; q < C::A_LOADS; ++q) {
+    const int gm = min(m0 + (wave * C::A_LOADS + q) * 8 + lr, T - 1);
+    a_src[q] = A + (size_t)gm * H + kbeg + lchunk * 8;
+  }
+#pragma unroll
+  for (int q = 0; q < C::B_LOADS; ++q)
+    b_src[q] = B + (size_t)(n0 + (wave * C::B_LOADS + q) * 8 + lr) * H + kbeg + lchunk * 8;
+
+  auto issue = [&](int s) {
+    uint8_t *base = smem + (s % NS) * C::STAGE_BYTES;
+#pragma unroll
+    for (int q = 0; q < C::A_LOADS; ++q)
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(a_src[q] + s * TK),
+                                       (lds_ptr_t)(base + (wave * C::A_LOADS + q) * 1024), 16, 0,
+                                       0);
+#pragma unroll
+    for (int q = 0; q < C::B_LOADS; ++q)
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(b_src[q] + s * TK),
+                                       (lds_ptr_t)(base + C::A_BYTES +
+                                                   (wave * C::B_LOADS + q) * 1024),
+                                       16, 0, 0);
+  };
+
+  Acc acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int v = 0; v < (int)(sizeof(Acc) / sizeof(float)); ++v) acc[i][j][v] = 0.f;
+
+  const int wm = (wave / C::WAVES_N) * C::WM, wn = (wave % C::WAVES_N) * C::WN;
+  // operand lane layout: row lane % MF of the MFMA tile, K run lane / MF
+  const int fr = lane % MF, fq = lane / MF;
+
+  // Fragments of one stage in registers, two sets: the next stage's
+  // fragments are read from LDS while the current stage's MFMAs run.
+  bf16x8 fa[2][C::KSTEPS][C::FM], fb[2][C::KSTEPS][C::FN];
+  auto read_frags = [&](int s, int set) {
+    const uint8_t *As = smem + (s % NS) * C::STAGE_BYTES;
+    const uint8_t *Bs = As + C::A_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) {
+      const int pos = ((ks * (C::KMF / 8) + fq) ^ (fr & 7)) * 16;
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+        fa[set][ks][i] = *reinterpret_cast<const bf16x8 *>(As + (wm + MF * i + fr) * 128 + pos);
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+        fb[set][ks][j] = *reinterpret_cast<const bf16x8 *>(Bs + (wn + MF * j + fr) * 128 + pos);
     }
   };
-  gload(kbeg);
-  for (int k0 = kbeg; k0 < kbeg + k_per_split; k0 += BK) {
-    __syncthreads();
+  auto mfmas = [&](int set) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int r = lr + 32 * h;
-      *reinterpret_cast<uint4 *>(&As[r * LDS_STRIDE + lc]) = ra[h];
-      *reinterpret_cast<uint4 *>(&Bs[r * LDS_STRIDE + lc]) = rb[h];
+    for (int ks = 0; ks < C::KSTEPS; ++ks)
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma(fa[set][ks][i], fb[set][ks][j], acc[i][j]);
+  };
+  // Wait until stage s has landed (only the later stages' loads may still be
+  // pending), then a barrier: every wave's part of stage s is in LDS, and
+  // every wave has finished reading the buffer the next issue overwrites.
+  auto stage_ready = [&](int s) {
+    wait_vmcnt_steps<C::LOADS, NS - 2>(min(NS - 2, nk - 1 - s));
+    stage_barrier();
+    if (s + NS - 1 < nk) issue(s + NS - 1);
+  };
+
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nk) issue(s);
+  stage_ready(0);
+  read_frags(0, 0);
+  // two stages per trip, so the register sets have constant indices
+  int s = 0;
+  for (; s + 1 < nk; s += 2) {
+    stage_ready(s + 1);
+    read_frags(s + 1, 1);
+    mfmas(0);
+    if (s + 2 < nk) {
+      stage_ready(s + 2);
+      read_frags(s + 2, 0);
     }
-    __syncthreads();
-    if (k0 + BK < kbeg + k_per_split) gload(k0 + BK);  // overlap with the MFMAs
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 32) {
-      bf16x8 a[2], b[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = *reinterpret_cast<const bf16x8 *>(&As[(wm + 16 * i + fr) * LDS_STRIDE + kk + fk]);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        b[j] = *reinterpret_cast<const bf16x8 *>(&Bs[(wn + 16 * j + fr) * LDS_STRIDE + kk + fk]);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
+    mfmas(1);
   }
-  // D[m = 4*(lane/16) + v][n = lane % 16] of each 16x16 tile
+  if (s < nk) mfmas(0);  // odd stage count: the last stage is in set 0
+
+  // D of one MFMA tile: 16x16: row 4*(lane/16) + v, column lane % 16;
+  // 32x32: row 8*(v/4) + 4*(lane/32) + v%4, column lane % 32.
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int tm = m0 + wm + 16 * i + 4 * (lane >> 4) + v;
-        const int en = n0 + wn + 16 * j + (lane & 15);
-        if (tm < T) Cs[(size_t)tm * E + en] = acc[i][j][v];
+      for (int v = 0; v < (int)(sizeof(Acc) / sizeof(float)); ++v) {
+        const int r = MF == 16 ? 4 * fq + v : 8 * (v / 4) + 4 * fq + (v % 4);
+        const int tm = m0 + wm + MF * i + r;
+        if (tm < T) Cs[(size_t)tm * E + n0 + wn + MF * j + fr] = acc[i][j][v];
       }
 }
 
-// out[i] = sum over s = 0..S-1 of part[s][i], in that order.
+// out[i] = sum over s = 0..S-1 of part[s][i], in that order; four
+// consecutive values per thread, the S partial loads issued together.
 __global__ __launch_bounds__(THREADS) void sum_splits_kernel(const float *__restrict__ part,
-                                                             int S, int64_t n,
+                                                             int S, int64_t n4,
                                                              float *__restrict__ out) {
-  for (int64_t i = (int64_t)blockIdx.x * THREADS + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * THREADS) {
-    float acc = part[i];
-    for (int s = 1; s < S; ++s) acc += part[(size_t)s * n + i];
-    out[i] = acc;
-  }
+  const int64_t i = (int64_t)blockIdx.x * THREADS + threadIdx.x;
+  if (i >= n4) return;
+  const float4 *p = reinterpret_cast<const float4 *>(part) + i;
+  float4 v[MAX_SPLITS];
+#pragma unroll
+  for (int s = 0; s < MAX_SPLITS; ++s)
+    if (s < S) v[s] = p[(size_t)s * n4];
+  float4 acc = v[0];
+#pragma unroll
+  for (int s = 1; s < MAX_SPLITS; ++s)
+    if (s < S) {
+      acc.x += v[s].x;
+      acc.y += v[s].y;
+      acc.z += v[s].z;
+      acc.w += v[s].w;
+    }
+  reinterpret_cast<float4 *>(out)[i] = acc;
+}
+
+struct Plan {
+  bool decode;
+  int m_tiles, n_tiles, splits;
+};
+
+// Tile shape by token count; then the K split: the largest divisor of
+// H / TK (at most MAX_SPLITS) that keeps the grid at or below about 256
+// blocks, one per compute unit.
+static Plan make_plan(int T, int E, int H) {
+  Plan pl;
+  pl.decode = T <= DECODE_MAX_T;
+  const int tm = pl.decode ? DecodeTile::TM : PrefillTile::TM;
+  const int tn = pl.decode ? DecodeTile::TN : PrefillTile::TN;
+  pl.m_tiles = (T + tm - 1) / tm;
+  pl.n_tiles = E / tn;
+  const int tiles = pl.m_tiles * pl.n_tiles;
+  int want = 256 / (tiles > 0 ? tiles : 1);
+  if (want > MAX_SPLITS) want = MAX_SPLITS;
+  const int kb = H / TK;
+  pl.splits = 1;
+  for (int d = 1; d <= want; ++d)
+    if (kb % d == 0) pl.splits = d;
+  return pl;
 }
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 static size_t partial_bytes(int T, int E, int H) {
-  const int S = pick_splits(T, E, H);
+  const int S = make_plan(T, E, H).splits;
   return S > 1 ? align256((size_t)S * T * E * sizeof(float)) : 0;
 }
 
@@ -151,7 +313,7 @@ size_t moe_router_gemm_route_workspace_bytes(int32_t num_tokens, int32_t hidden,
     return 0;
   const size_t r = (moe_route_workspace_bytes(num_tokens, num_experts_out, top_k) + 255) &
                    ~(size_t)255;
-  if (hidden % moe_gemm::BK != 0 || num_experts % moe_gemm::BN != 0) return r;
+  if (hidden % moe_gemm::TK != 0 || num_experts % moe_gemm::PrefillTile::TN != 0) return r;
   return r + moe_gemm::partial_bytes(num_tokens, num_experts, hidden);
 }
 
@@ -165,9 +327,11 @@ int moe_router_gemm_route(const uint16_t *hidden_bf16, const uint16_t *weight_bf
   if (!params || !out) return MOE_ERR_NULL;
   const int T = num_tokens, H = hidden, E = params->num_experts;
   if (T < 0 || H <= 0 || E <= 0 || params->top_k <= 0) return MOE_ERR_SHAPE;
-  if (H % BK != 0 || E % BN != 0) return MOE_ERR_UNSUPPORTED;
+  if (H % TK != 0 || E % PrefillTile::TN != 0) return MOE_ERR_UNSUPPORTED;
   if (T > 0 && (!hidden_bf16 || !weight_bf16 || !logits_out)) return MOE_ERR_NULL;
-  if (((uintptr_t)hidden_bf16 | (uintptr_t)weight_bf16) % 16 != 0) return MOE_ERR_SHAPE;
+  if (((uintptr_t)hidden_bf16 | (uintptr_t)weight_bf16 | (uintptr_t)logits_out) % 16 != 0)
+    return MOE_ERR_SHAPE;
+  if ((uintptr_t)workspace % 16 != 0) return MOE_ERR_WORKSPACE;
   const int32_t e_local =
       moe_route_local_num_experts(E, params->top_k, local_expert_offset, num_local_experts);
   if (e_local < 0) return e_local;
@@ -184,18 +348,23 @@ int moe_router_gemm_route(const uint16_t *hidden_bf16, const uint16_t *weight_bf
                              ~(size_t)255;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (T > 0) {
-    const int S = pick_splits(T, E, H);
+    const Plan pl = make_plan(T, E, H);
+    const int S = pl.splits;
     float *dst = S > 1 ? reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) +
                                                    route_bytes)
                        : logits_out;
-    dim3 grid(E / BN, (T + BM - 1) / BM, S);
-    router_gemm_kernel<<<grid, THREADS, 0, st>>>(hidden_bf16, weight_bf16, dst, T, E, H, H / S);
+    const int blocks = pl.m_tiles * pl.n_tiles * S;
+    if (pl.decode)
+      router_gemm_kernel<DecodeTile><<<blocks, THREADS, 0, st>>>(
+          hidden_bf16, weight_bf16, dst, T, E, H, H / S, pl.m_tiles, pl.n_tiles);
+    else
+      router_gemm_kernel<PrefillTile><<<blocks, THREADS, 0, st>>>(
+          hidden_bf16, weight_bf16, dst, T, E, H, H / S, pl.m_tiles, pl.n_tiles);
     if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
     if (S > 1) {
-      const int64_t n = (int64_t)T * E;
-      int64_t g = (n + THREADS * 4 - 1) / (THREADS * 4);
-      if (g > 4096) g = 4096;
-      sum_splits_kernel<<<(int)g, THREADS, 0, st>>>(dst, S, n, logits_out);
+      const int64_t n4 = (int64_t)T * E / 4;
+      const int64_t g = (n4 + THREADS - 1) / THREADS;
+      sum_splits_kernel<<<(int)g, THREADS, 0, st>>>(dst, S, n4, logits_out);
       if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
     }
   }

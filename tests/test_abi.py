@@ -132,6 +132,7 @@ def test_router_gemm_validation(L):
     assert call(off=890, cnt=10) == ERR_RANGE
     assert call(p=_params(N=3)) == ERR_UNSUP  # routing args checked before any launch
     assert call(hidden=FAKE + 2) == ERR_SHAPE
+    assert call(logits=FAKE + 8) == ERR_SHAPE   # logits 16-byte aligned
 
 
 def test_sigmoid_validation(L):

@@ -89,7 +89,7 @@ def test_long_prefill_32k_full():
     assert load.max() / load.mean() > 7.0
 
 
-@pytest.mark.parametrize("T", [64, 4096])
+@pytest.mark.parametrize("T", [1, 64, 100, 129, 1000, 4096])
 def test_router_gemm_then_route(T):
     c = W.router_case(T)
     say(f"case router_gemm T={T}")
