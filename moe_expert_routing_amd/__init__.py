@@ -92,16 +92,29 @@ def _check(status: int, what: str) -> None:
         raise MoeRouteError(f"{what} failed: {msg} ({status})")
 
 
+_E_OUT: Dict[tuple, int] = {}
+
+
 def local_num_experts(num_experts: int, top_k: int, local_expert_offset: int,
                       num_local_experts: int) -> int:
-    v = lib().moe_route_local_num_experts(num_experts, top_k, local_expert_offset,
-                                          num_local_experts)
-    if v < 0:
-        _check(v, "moe_route_local_num_experts")
-    return int(v)
+    key = (num_experts, top_k, local_expert_offset, num_local_experts)
+    v = _E_OUT.get(key)
+    if v is None:
+        v = int(lib().moe_route_local_num_experts(*key))
+        if v < 0:
+            _check(v, "moe_route_local_num_experts")
+        _E_OUT[key] = v
+    return v
+
+
+_RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 def _stream_handle(device: torch.device) -> int:
+    """The current HIP stream of `device` as an integer handle."""
+    idx = device.index
+    if _RAW_STREAM is not None and idx is not None:
+        return _RAW_STREAM(idx)
     return torch.cuda.current_stream(device).cuda_stream
 
 
@@ -134,12 +147,24 @@ def alloc_outputs(T: int, top_k: int, e_out: int, device: torch.device,
     return out
 
 
+_OUTPUT_NAMES = ("topk_ids", "topk_weights", "packed", "counts", "offsets", "perm", "inv_perm")
+_PRM_CACHE: Dict[tuple, tuple] = {}  # params struct (and its byref) per shape
+
+
 def _outputs_struct(out: Dict[str, torch.Tensor]) -> RouteOutputs:
     def p(name):
         t = out.get(name)
         return t.data_ptr() if t is not None and t.numel() > 0 else None
-    return RouteOutputs(p("topk_ids"), p("topk_weights"), p("packed"), p("counts"),
-                        p("offsets"), p("perm"), p("inv_perm"))
+    return RouteOutputs(*(p(n) for n in _OUTPUT_NAMES))
+
+
+def _params_ref(E, n_groups, topk_group, top_k, group_topn):
+    key = (E, n_groups, topk_group, top_k, group_topn)
+    hit = _PRM_CACHE.get(key)
+    if hit is None:
+        prm = RouteParams(*key)
+        hit = _PRM_CACHE[key] = (prm, ctypes.byref(prm))
+    return hit
 
 
 def _require(t: torch.Tensor, name: str, dtype, ndim: int) -> None:
@@ -169,15 +194,15 @@ def route_local(logits: torch.Tensor, bias: torch.Tensor, local_expert_offset: i
     dev = logits.device
     if out is None:
         out = alloc_outputs(T, top_k, e_out, dev)
-    need = lib().moe_route_workspace_bytes(T, e_out, top_k)
-    if ws is None:
-        ws = workspace(dev, need)
-    prm = _params(E, n_groups, topk_group, top_k, group_topn)
+    if ws is None:  # a caller's workspace is checked by the library itself
+        ws = workspace(dev, lib().moe_route_workspace_bytes(T, e_out, top_k))
+    prm = _params_ref(E, n_groups, topk_group, top_k, group_topn)
     o = _outputs_struct(out)
-    st = lib().moe_route_local(logits.data_ptr(), bias.data_ptr(), T, ctypes.byref(prm),
+    st = lib().moe_route_local(logits.data_ptr(), bias.data_ptr(), T, prm[1],
                                local_expert_offset, num_local_experts, ctypes.byref(o),
                                ws.data_ptr(), ws.numel(), _stream_handle(dev))
-    _check(st, "moe_route_local")
+    if st:
+        _check(st, "moe_route_local")
     out["num_experts_out"] = e_out
     return out
 
@@ -192,13 +217,12 @@ def route(logits: torch.Tensor, bias: torch.Tensor, *, n_groups: int = 8, topk_g
     dev = logits.device
     if out is None:
         out = alloc_outputs(T, top_k, E, dev)
-    need = lib().moe_route_workspace_bytes(T, E, top_k)
-    if ws is None:
-        ws = workspace(dev, need)
-    prm = _params(E, n_groups, topk_group, top_k, group_topn)
+    if ws is None:  # a caller's workspace is checked by the library itself
+        ws = workspace(dev, lib().moe_route_workspace_bytes(T, E, top_k))
+    prm = _params_ref(E, n_groups, topk_group, top_k, group_topn)
     o = _outputs_struct(out)
-    st = lib().moe_route(logits.data_ptr(), bias.data_ptr(), T, ctypes.byref(prm),
-                         ctypes.byref(o), ws.data_ptr(), ws.numel(), _stream_handle(dev))
+    st = lib().moe_route(logits.data_ptr(), bias.data_ptr(), T, prm[1], ctypes.byref(o),
+                         ws.data_ptr(), ws.numel(), _stream_handle(dev))
     _check(st, "moe_route")
     out["num_experts_out"] = E
     return out

@@ -49,22 +49,32 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
   return v;
 }
 
-// Exclusive scan of in[0..n) (n <= 1024, any memory) into out[0..n] in LDS,
-// out[n] = total. All BLOCK threads must call it.
-__device__ void block_exclusive_scan(const int32_t *in, int n, int32_t *out, int32_t *wave_tot) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wv = tid >> 6;
-  int v[4];
-  int s = 0;
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// accesses, not for its global loads still in flight (a __syncthreads()
+// waits for every outstanding load).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Exclusive scan of in[0..n) (n <= 1024) into out[0..n] in LDS, out[n] =
+// total, in two steps so that a caller can issue other loads between them:
+// scan_load reads this thread's 4 inputs; scan_store scans and writes.
+// All BLOCK threads must call both.
+__device__ __forceinline__ void scan_load(const int32_t *in, int n, int (&v)[4]) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const int idx = tid * 4 + k;
+    const int idx = threadIdx.x * 4 + k;
     v[k] = idx < n ? in[idx] : 0;
-    s += v[k];
   }
+}
+__device__ __forceinline__ void scan_store(const int (&v)[4], int n, int32_t *out,
+                                           int32_t *wave_tot) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int s = v[0] + v[1] + v[2] + v[3];
   const int incl = wave_inclusive_scan(s);
   if (lane == 63) wave_tot[wv] = incl;
-  __syncthreads();
+  lds_barrier();
   int wave_off = 0;
   for (int w = 0; w < wv; ++w) wave_off += wave_tot[w];
   int run = wave_off + incl - s;
@@ -75,7 +85,15 @@ __device__ void block_exclusive_scan(const int32_t *in, int n, int32_t *out, int
     run += v[k];
   }
   if (tid == BLOCK - 1) out[n] = wave_off + incl;
-  __syncthreads();
+  lds_barrier();
+}
+
+// The same in one call (in may be LDS or global memory; in place allowed:
+// every read precedes every write).
+__device__ void block_exclusive_scan(const int32_t *in, int n, int32_t *out, int32_t *wave_tot) {
+  int v[4];
+  scan_load(in, n, v);
+  scan_store(v, n, out, wave_tot);
 }
 
 // ---------------------------------------------------------------------------
@@ -340,6 +358,9 @@ __global__ __launch_bounds__(BLOCK) void scatter_kernel(
   __shared__ int32_t offs[MOE_ROUTE_MAX_EXPERTS + 1];
   __shared__ int32_t wave_tot[WAVES_PER_BLOCK];
   const int64_t f0 = (int64_t)blockIdx.x * BLOCK * SCATTER_PER_THREAD + threadIdx.x;
+  // counts first: the offsets scan then overlaps the entry loads
+  int cv[4];
+  scan_load(counts, e_out, cv);
   int ev[SCATTER_PER_THREAD], rv[SCATTER_PER_THREAD];
 #pragma unroll
   for (int k = 0; k < SCATTER_PER_THREAD; ++k) {
@@ -353,7 +374,7 @@ __global__ __launch_bounds__(BLOCK) void scatter_kernel(
     const int64_t f = f0 + (int64_t)k * BLOCK;
     hv[k] = f < n ? hist[(size_t)ev[k] * nblk + (int)((f / K) / tokens_per_blk)] : 0;
   }
-  block_exclusive_scan(counts, e_out, offs, wave_tot);
+  scan_store(cv, e_out, offs, wave_tot);
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i <= e_out; i += BLOCK) offsets[i] = offs[i];
 #pragma unroll
