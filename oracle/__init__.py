@@ -11,6 +11,8 @@ from .route_ref import (  # noqa: F401
     exclusive_offsets,
     expert_counts,
     expert_major_permutation,
+    grouped_layout,
+    grouped_layout_rows,
     group_scores,
     kept_groups,
     local_num_experts,

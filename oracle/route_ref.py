@@ -256,6 +256,45 @@ def expert_major_permutation(ids_out: np.ndarray, e_out: int) -> Tuple[np.ndarra
 
 
 # ----------------------------------------------------------------------------
+# Grouped-GEMM layout (the next consumer of counts and perm)
+# ----------------------------------------------------------------------------
+# The pages say only that an expert-parallel backend builds the per-row
+# expert index array of a grouped GEMM from the routing ("Add MoonEP
+# expert-parallel arm of the Kimi-K3 B300 agentic sweep", the review summary
+# of the patch: its prepare/finalize step). The plainest reading
+# of such a layout, taken here: the entries of output id e occupy rows
+# padded_offsets[e] .. padded_offsets[e] + counts[e] - 1 in permutation
+# order, then padding rows up to padded_offsets[e+1] = padded_offsets[e] +
+# round_up(counts[e], tile_m); each row's expert index is e, or -1 on a
+# padding row; each row's entry is the flat index f = t*K + k it holds, or -1.
+# Rows past padded_offsets[E'] (up to the caller's row count) are -1.
+
+
+def grouped_layout_rows(n_entries: int, e_out: int, tile_m: int) -> int:
+    """Upper bound on the padded row count: every id wastes < tile_m rows."""
+    return n_entries + e_out * (tile_m - 1)
+
+
+def grouped_layout(counts: np.ndarray, perm: np.ndarray, tile_m: int,
+                   rows: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    counts = [int(c) for c in counts]
+    e_out = len(counts)
+    padded = np.zeros(e_out + 1, dtype=np.int64)
+    for e in range(e_out):
+        padded[e + 1] = padded[e] + -(-counts[e] // tile_m) * tile_m
+    m_indices = np.full(rows, -1, dtype=np.int64)
+    row_entry = np.full(rows, -1, dtype=np.int64)
+    p = 0  # position in perm: entries of id e are perm[p .. p + counts[e])
+    for e in range(e_out):
+        for j in range(counts[e]):
+            r = int(padded[e]) + j
+            m_indices[r] = e
+            row_entry[r] = int(perm[p + j])
+        p += counts[e]
+    return padded.astype(np.int32), m_indices.astype(np.int32), row_entry.astype(np.int32)
+
+
+# ----------------------------------------------------------------------------
 # The whole step
 # ----------------------------------------------------------------------------
 
