@@ -7,7 +7,8 @@ workload: 32768 tokens x 896 fp32 logits, Zipf-skewed bias, rank range
 [0, 112) -> 128 output ids. Inputs rotate over three seeded sets (3 x 117 MB
 of logits) so they cannot be served from the 256 MB last-level cache.
 
-Also reported: decode latency (us per call at 8, 16 and 64 tokens, eager and
+Also reported: the grouped-GEMM layout of the step's entries (us per call),
+decode latency (us per call at 8, 16 and 64 tokens, eager and
 replayed from a HIP graph), the router GEMM + route at 64 and 4096 tokens,
 the roofline of the route kernel (timed live with HIP events on the launch
 stream), and the CPU oracle timed on a bounded sample of the same workload.
@@ -269,6 +270,28 @@ def main():
             decode_graph[f"T{Td}"] = f"unavailable: {type(exc).__name__}"
 
     # ------------------------------------------------------------------
+    # grouped-GEMM layout of the long-prefill step's entries (tile 128): us
+    # per call (eager and replayed from a HIP graph) and GB/s over its
+    # algorithmic bytes (counts, perm, padded offsets, m_indices and
+    # row_entry over the bound row count)
+    # ------------------------------------------------------------------
+    log("bench: grouped-GEMM layout")
+    grouped = {}
+    for tile in (128,):
+        lay = M.grouped_layout(out["counts"], out["perm"], tile)
+        rows = lay["m_indices"].shape[0]
+        n_ent = out["perm"].shape[0]
+        gl_bytes = 4 * e_out + 4 * n_ent + 4 * (e_out + 1) + 8 * rows
+        gl_fn = (lambda tile=tile, lay=lay:
+                 M.grouped_layout(out["counts"], out["perm"], tile, out=lay))
+        gl_fn()
+        gl_us = time_calls(gl_fn, 200)
+        gl_graph_us = time_graph(gl_fn, 200)
+        grouped[f"tile{tile}"] = {"us_per_call": round(gl_us, 2),
+                                  "us_per_call_hipgraph": round(gl_graph_us, 2), "rows": rows,
+                                  "gbps_hipgraph": round(gl_bytes / (gl_graph_us * 1e-6) / 1e9, 1)}
+
+    # ------------------------------------------------------------------
     # router GEMM + route
     # ------------------------------------------------------------------
     gemm = {}
@@ -338,6 +361,7 @@ def main():
         "empty_kernel_us_per_call": floor,
         "decode_us_per_call_hipgraph": decode_graph,
         "router_gemm_route": gemm,
+        "grouped_layout_32768": grouped,
         "roofline": {"bound": "hbm", "kernel": "route_rows_kernel",
                      "achieved": round(kern_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(frac, 4),

@@ -166,6 +166,37 @@ int moe_router_gemm_route(const uint16_t *hidden_bf16,
                           size_t workspace_bytes, void *stream);
 
 /*
+ * Grouped-GEMM layout of a routing call's entries, the index arrays a
+ * contiguous grouped GEMM over the experts consumes (an expert-parallel
+ * backend builds them after routing: "Add MoonEP expert-parallel arm of the
+ * Kimi-K3 B300 agentic sweep", review summary of the patch, its
+ * prepare/finalize step). From counts [E'] and perm [n_entries] of one
+ * routing call (same stream, so the call has finished writing them):
+ *   padded_offsets [E'+1]: padded[0] = 0, padded[e+1] = padded[e] +
+ *       round_up(counts[e], tile_m);
+ *   m_indices [rows]: row padded[e] + j holds id e for j < counts[e] and -1
+ *       on the padding rows after it; rows from padded[E'] on are -1;
+ *   row_entry [rows] (nullable): the flat entry f = t*K + k of each real
+ *       row, perm[offsets[e] + j] (ascending within an id), -1 elsewhere.
+ * rows must be at least moe_grouped_layout_rows(n_entries, E', tile_m), the
+ * padded total when every id wastes tile_m - 1 rows (the actual total,
+ * padded[E'], is only known on the device). Device pointers owned by the
+ * caller; asynchronous on stream; nothing is allocated. Checked on the host
+ * before any launch: NULL pointers (perm may be NULL when n_entries == 0,
+ * m_indices when rows == 0) -> MOE_ERR_NULL; 1 <= E' <= 1024,
+ * 1 <= tile_m <= MOE_GROUPED_MAX_TILE, 0 <= n_entries <=
+ * MOE_GROUPED_MAX_ENTRIES, rows too small -> MOE_ERR_SHAPE. counts must
+ * sum to n_entries (as a routing call's do); if they do not, the rows are
+ * wrong but every access stays inside the arrays.
+ */
+#define MOE_GROUPED_MAX_TILE 4096
+#define MOE_GROUPED_MAX_ENTRIES (1 << 30)
+int64_t moe_grouped_layout_rows(int64_t n_entries, int32_t num_experts_out, int32_t tile_m);
+int moe_grouped_layout(const int32_t *counts, const int32_t *perm, int32_t num_experts_out,
+                       int64_t n_entries, int32_t tile_m, int32_t *padded_offsets,
+                       int32_t *m_indices, int32_t *row_entry, int64_t rows, void *stream);
+
+/*
  * Diagnostic: y[i] = the binary32 nearest to 1 / (1 + e^-x[i]) for n
  * elements, with the routing kernels' own sigmoid. mode 0 = the production
  * evaluation; mode 1 = the double-double re-evaluation only (the path taken

@@ -12,6 +12,8 @@ Calls (same names as the C ABI):
     route_local(logits, bias, off, cnt, ...)       -> moe_route_local
     router_gemm_route(hidden, weight, bias, ...)   -> moe_router_gemm_route
     local_num_experts(E, K, off, cnt)              -> moe_route_local_num_experts
+    grouped_layout(counts, perm, tile_m, ...)      -> moe_grouped_layout
+    grouped_layout_rows(n_entries, E', tile_m)     -> moe_grouped_layout_rows
     sigmoid_rn32(x, mode=0)                        -> moe_sigmoid_rn32 (diagnostic)
 """
 from __future__ import annotations
@@ -61,6 +63,9 @@ EXPORTS = {
     "moe_route_set_kernel_events": (ctypes.c_int, [_c_vp, _c_vp]),
     "moe_route_exact_path_tokens": (ctypes.c_int64, [_c_i32]),
     "moe_route_path_tokens": (ctypes.c_int64, [_c_i32, _c_i32]),
+    "moe_grouped_layout_rows": (ctypes.c_int64, [ctypes.c_int64, _c_i32, _c_i32]),
+    "moe_grouped_layout": (ctypes.c_int, [_c_vp, _c_vp, _c_i32, ctypes.c_int64, _c_i32, _c_vp,
+                                          _c_vp, _c_vp, ctypes.c_int64, _c_vp]),
 }
 
 _LIB = None
@@ -293,6 +298,41 @@ def path_tokens(path: int, reset: bool = False) -> int:
     if v < 0:
         _check(int(v), "moe_route_path_tokens")
     return int(v)
+
+
+def grouped_layout_rows(n_entries: int, num_experts_out: int, tile_m: int) -> int:
+    v = lib().moe_grouped_layout_rows(n_entries, num_experts_out, tile_m)
+    if v < 0:
+        _check(int(v), "moe_grouped_layout_rows")
+    return int(v)
+
+
+def grouped_layout(counts: torch.Tensor, perm: torch.Tensor, tile_m: int, *,
+                   rows: Optional[int] = None, with_entries: bool = True,
+                   out: Optional[Dict[str, torch.Tensor]] = None) -> Dict[str, torch.Tensor]:
+    """moe_grouped_layout over a routing call's counts [E'] and perm [T*K]:
+    padded_offsets [E'+1], m_indices [rows] and (with_entries) row_entry
+    [rows]. rows defaults to the bound moe_grouped_layout_rows."""
+    _require(counts, "counts", torch.int32, 1)
+    _require(perm, "perm", torch.int32, 1)
+    e_out, n = counts.shape[0], perm.shape[0]
+    need = grouped_layout_rows(n, e_out, tile_m)
+    rows = need if rows is None else rows
+    dev = counts.device
+    if out is None:
+        out = {"padded_offsets": torch.empty(e_out + 1, dtype=torch.int32, device=dev),
+               "m_indices": torch.empty(rows, dtype=torch.int32, device=dev)}
+        if with_entries:
+            out["row_entry"] = torch.empty(rows, dtype=torch.int32, device=dev)
+    re = out.get("row_entry")
+    st = lib().moe_grouped_layout(counts.data_ptr(), perm.data_ptr() if n else None, e_out, n,
+                                  tile_m, out["padded_offsets"].data_ptr(),
+                                  out["m_indices"].data_ptr() if rows else None,
+                                  re.data_ptr() if re is not None and rows else None, rows,
+                                  _stream_handle(dev))
+    if st:
+        _check(st, "moe_grouped_layout")
+    return out
 
 
 def sigmoid_rn32(x: torch.Tensor, mode: int = 0) -> torch.Tensor:

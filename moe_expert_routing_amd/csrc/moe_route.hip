@@ -388,6 +388,76 @@ __global__ __launch_bounds__(BLOCK) void scatter_kernel(
   }
 }
 
+// Grouped-GEMM layout from a routing call's counts and perm: the entries of
+// id e fill rows padded[e] .. padded[e] + counts[e] - 1 in permutation order,
+// then padding rows up to padded[e+1] = padded[e] + round_up(counts[e],
+// tile_m). Every block forms both scans of counts in LDS (E' <= 1024);
+// block 0 writes the padded offsets; each thread fills LAYOUT_PER_THREAD
+// consecutive rows (one 16-byte store per array when aligned), finding the
+// first row's id by binary search over the padded offsets. Reads
+// of perm and writes of rows are bounds-checked, so counts that do not
+// match perm give wrong rows but no access outside the arrays.
+constexpr int LAYOUT_PER_THREAD = 4;  // the int4 stores below assume 4
+
+__global__ __launch_bounds__(BLOCK) void grouped_layout_kernel(
+    const int32_t *__restrict__ counts, const int32_t *__restrict__ perm, int e_out,
+    int64_t n_entries, int tile_m, int32_t *__restrict__ padded_offsets,
+    int32_t *__restrict__ m_indices, int32_t *__restrict__ row_entry, int64_t rows) {
+  __shared__ int32_t offs[MOE_ROUTE_MAX_EXPERTS + 1];
+  __shared__ int32_t pad[MOE_ROUTE_MAX_EXPERTS + 1];
+  __shared__ int32_t wave_tot[WAVES_PER_BLOCK];
+  int cv[4], pv[4];
+  scan_load(counts, e_out, cv);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    cv[k] = max(cv[k], 0);
+    pv[k] = (cv[k] + tile_m - 1) / tile_m * tile_m;
+  }
+  scan_store(cv, e_out, offs, wave_tot);
+  scan_store(pv, e_out, pad, wave_tot);
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i <= e_out; i += BLOCK) padded_offsets[i] = pad[i];
+  // this thread's LAYOUT_PER_THREAD consecutive rows: one binary search for
+  // the first (the largest e with pad[e] <= r; pad[0] = 0), then step
+  const int64_t r0 = ((int64_t)blockIdx.x * BLOCK + threadIdx.x) * LAYOUT_PER_THREAD;
+  if (r0 >= rows) return;
+  int lo = 0, hi = e_out + 1;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if ((int64_t)pad[mid] <= r0) lo = mid;
+    else hi = mid;
+  }
+  int32_t mi[LAYOUT_PER_THREAD], ent[LAYOUT_PER_THREAD];
+#pragma unroll
+  for (int k = 0; k < LAYOUT_PER_THREAD; ++k) {
+    const int64_t r = r0 + k;
+    while (lo < e_out && (int64_t)pad[lo + 1] <= r) ++lo;
+    mi[k] = -1;
+    ent[k] = -1;
+    if (lo < e_out) {
+      const int64_t j = r - pad[lo];
+      if (j < (int64_t)(offs[lo + 1] - offs[lo])) {
+        const int64_t idx = offs[lo] + j;
+        mi[k] = lo;
+        ent[k] = (idx >= 0 && idx < n_entries) ? perm[idx] : -1;
+      }
+    }
+  }
+  if (r0 + LAYOUT_PER_THREAD <= rows && ((uintptr_t)(m_indices + r0) & 15) == 0 &&
+      (!row_entry || ((uintptr_t)(row_entry + r0) & 15) == 0)) {
+    *reinterpret_cast<int4 *>(m_indices + r0) = make_int4(mi[0], mi[1], mi[2], mi[3]);
+    if (row_entry)
+      *reinterpret_cast<int4 *>(row_entry + r0) = make_int4(ent[0], ent[1], ent[2], ent[3]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < LAYOUT_PER_THREAD; ++k) {
+      if (r0 + k >= rows) break;
+      m_indices[r0 + k] = mi[k];
+      if (row_entry) row_entry[r0 + k] = ent[k];
+    }
+  }
+}
+
 // Diagnostic sigmoid kernel.
 __global__ void sigmoid_kernel(const float *__restrict__ x, float *__restrict__ y, int64_t n,
                                int mode) {
@@ -550,7 +620,7 @@ static int route_impl(const float *logits, const float *bias, int32_t T,
 
 extern "C" {
 
-int32_t moe_route_abi_version(void) { return 100; }
+int32_t moe_route_abi_version(void) { return 101; }
 
 const char *moe_route_status_string(int status) {
   switch (status) {
@@ -630,6 +700,31 @@ int moe_route_set_kernel_events(void *before, void *after) {
   moe::g_ev_before = reinterpret_cast<hipEvent_t>(before);
   moe::g_ev_after = reinterpret_cast<hipEvent_t>(after);
   return MOE_OK;
+}
+
+int64_t moe_grouped_layout_rows(int64_t n_entries, int32_t num_experts_out, int32_t tile_m) {
+  if (n_entries < 0 || n_entries > MOE_GROUPED_MAX_ENTRIES) return MOE_ERR_SHAPE;
+  if (num_experts_out < 1 || num_experts_out > MOE_ROUTE_MAX_EXPERTS) return MOE_ERR_SHAPE;
+  if (tile_m < 1 || tile_m > MOE_GROUPED_MAX_TILE) return MOE_ERR_SHAPE;
+  return n_entries + (int64_t)num_experts_out * (tile_m - 1);
+}
+
+int moe_grouped_layout(const int32_t *counts, const int32_t *perm, int32_t num_experts_out,
+                       int64_t n_entries, int32_t tile_m, int32_t *padded_offsets,
+                       int32_t *m_indices, int32_t *row_entry, int64_t rows, void *stream) {
+  const int64_t need = moe_grouped_layout_rows(n_entries, num_experts_out, tile_m);
+  if (need < 0) return (int)need;
+  if (!counts || !padded_offsets || (n_entries > 0 && !perm)) return MOE_ERR_NULL;
+  if (rows < need) return MOE_ERR_SHAPE;
+  if (rows > 0 && !m_indices) return MOE_ERR_NULL;
+  const int64_t per_block = (int64_t)moe::BLOCK * moe::LAYOUT_PER_THREAD;
+  const int64_t grid = rows > 0 ? (rows + per_block - 1) / per_block : 1;
+  if (grid > INT32_MAX) return MOE_ERR_SHAPE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  moe::grouped_layout_kernel<<<(int)grid, moe::BLOCK, 0, st>>>(
+      counts, perm, num_experts_out, n_entries, tile_m, padded_offsets, m_indices, row_entry,
+      rows);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 int moe_sigmoid_rn32(const float *x, float *y, int64_t n, int32_t mode, void *stream) {

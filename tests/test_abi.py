@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.moe_route_abi_version() == 100
+    assert L.moe_route_abi_version() == 101
     for code in (OK, ERR_NULL, ERR_SHAPE, ERR_RANGE, ERR_UNSUP, ERR_WS, ERR_HIP):
         assert L.moe_route_status_string(code)
     assert L.moe_route_status_string(-99) == b"unknown status"
@@ -133,6 +133,27 @@ def test_router_gemm_validation(L):
     assert call(p=_params(N=3)) == ERR_UNSUP  # routing args checked before any launch
     assert call(hidden=FAKE + 2) == ERR_SHAPE
     assert call(logits=FAKE + 8) == ERR_SHAPE   # logits 16-byte aligned
+
+
+def test_grouped_layout_validation(L):
+    assert L.moe_grouped_layout_rows(100, 128, 64) == 100 + 128 * 63
+    assert L.moe_grouped_layout_rows(0, 896, 1) == 0
+    assert L.moe_grouped_layout_rows(-1, 128, 64) == ERR_SHAPE
+    assert L.moe_grouped_layout_rows(10, 0, 64) == ERR_SHAPE
+    assert L.moe_grouped_layout_rows(10, 1025, 64) == ERR_SHAPE
+    assert L.moe_grouped_layout_rows(10, 128, 0) == ERR_SHAPE
+    assert L.moe_grouped_layout_rows(10, 128, 4097) == ERR_SHAPE
+    assert L.moe_grouped_layout_rows((1 << 30) + 1, 128, 64) == ERR_SHAPE
+    def call(counts=FAKE, perm=FAKE, E=128, n=100, tile=64, po=FAKE, mi=FAKE, re=FAKE, rows=None):
+        rows = 100 + 128 * 63 if rows is None else rows
+        return L.moe_grouped_layout(counts, perm, E, n, tile, po, mi, re, rows, None)
+    assert call(counts=None) == ERR_NULL
+    assert call(perm=None) == ERR_NULL
+    assert call(po=None) == ERR_NULL
+    assert call(mi=None) == ERR_NULL
+    assert call(rows=100 + 128 * 63 - 1) == ERR_SHAPE
+    assert call(tile=0) == ERR_SHAPE
+    assert call(E=0) == ERR_SHAPE
 
 
 def test_sigmoid_validation(L):
