@@ -13,6 +13,9 @@ from .route_ref import (  # noqa: F401
     expert_major_permutation,
     grouped_layout,
     grouped_layout_rows,
+    e4m3_code,
+    e4m3_value,
+    mxfp8_quantize,
     group_scores,
     kept_groups,
     local_num_experts,

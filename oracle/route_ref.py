@@ -37,7 +37,11 @@ rounding and the renormalisation. This oracle takes the plainest readings:
 * weights: the unbiased s of the selected experts divided by their sum,
   evaluated in binary64 (exact sum via math.fsum) and rounded to binary32;
 * bf16: round-to-nearest-even of the binary32 weight;
-* within one expert, entries are ordered by ascending flat index t*top_k+k.
+* within one expert, entries are ordered by ascending flat index t*top_k+k;
+* grouped-GEMM layout (a consumer of counts and perm): each id's entries in
+  permutation order from its tile-padded offset, padding rows marked -1;
+* activations of the fused route + quant launch: OCP MXFP8 (E4M3 elements,
+  one E8M0 scale per 32 elements), round to nearest even, saturating.
 
 Every function below has a pin in ``tests/test_oracle_*.py`` (brute force,
 library routines, closed forms, mpmath, and the value the pages print).
@@ -292,6 +296,79 @@ def grouped_layout(counts: np.ndarray, perm: np.ndarray, tile_m: int,
             row_entry[r] = int(perm[p + j])
         p += counts[e]
     return padded.astype(np.int32), m_indices.astype(np.int32), row_entry.astype(np.int32)
+
+
+# ----------------------------------------------------------------------------
+# Activation quantisation of the fused route + quant launch (MXFP8)
+# ----------------------------------------------------------------------------
+# The pages name a fused route + quant launch for decode batches of up to 64
+# tokens whose routed MoE runs MXFP4 expert weights ("[kimi-k3] Rank-local
+# expert ids for the EP routed MoE (upstream #45544)", commit message), but
+# not the activation format. Reading taken: OCP MXFP8 with E4M3 elements,
+# one E8M0 scale per 32 consecutive elements of a token's hidden row:
+#   shared = floor(log2(amax)) - 8   (8 = the largest E4M3 exponent),
+#            at least -127; a block of zeros gets shared = -127;
+#   scale code = shared + 127 (E8M0: the scale is 2^shared);
+#   element = E4M3 code of v / 2^shared, rounded to nearest (ties to even)
+#             and saturated at +-448 (E4M3 without infinities, max 448).
+
+MX_BLOCK = 32
+E4M3_MAX = 448.0
+
+
+def e4m3_code(q: float) -> int:
+    """OCP E4M3 code of the real q: round to nearest, ties to even, saturate
+    at +-448; the sign of zero is kept."""
+    neg = math.copysign(1.0, q) < 0
+    a = abs(q)
+    if a >= E4M3_MAX:
+        code = 0x7E
+    else:
+        # quantum of a's binade (exponent at least -6: the subnormal step is 2^-9)
+        e = max(math.frexp(a)[1] - 1, -6) if a > 0 else -6
+        quantum = 2.0 ** (e - 3)
+        k = a / quantum                    # exact: a is a binary64 multiple of 2^-200
+        n = math.floor(k)
+        frac = k - n
+        if frac > 0.5 or (frac == 0.5 and n % 2 == 1):
+            n += 1
+        r = n * quantum                    # the rounded magnitude, <= 448
+        if r == 0:
+            code = 0
+        elif r < 2.0 ** -6:                # subnormal: mantissa = r / 2^-9
+            code = int(round(r / 2.0 ** -9))
+        else:
+            ee = math.frexp(r)[1] - 1      # binade of the rounded value
+            mant = int(round((r / 2.0 ** ee - 1.0) * 8))
+            code = ((ee + 7) << 3) | mant
+    return code | (0x80 if neg else 0)
+
+
+def e4m3_value(code: int) -> float:
+    """Real value of an E4M3 code (0x7F / 0xFF, the NaN codes, excluded)."""
+    sign = -1.0 if code & 0x80 else 1.0
+    ef, mf = (code >> 3) & 0xF, code & 7
+    if ef == 0:
+        return sign * mf * 2.0 ** -9
+    return sign * (1.0 + mf / 8.0) * 2.0 ** (ef - 7)
+
+
+def mxfp8_quantize(hidden_bits: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """bf16 hidden [T, H] (bit patterns, H a multiple of 32) -> E4M3 codes
+    uint8 [T, H] and E8M0 scale codes uint8 [T, H / 32]."""
+    v = bf16_bits_to_f64(hidden_bits)
+    T, H = v.shape
+    codes = np.zeros((T, H), dtype=np.uint8)
+    scales = np.zeros((T, H // MX_BLOCK), dtype=np.uint8)
+    for t in range(T):
+        for b in range(H // MX_BLOCK):
+            blk = v[t, b * MX_BLOCK:(b + 1) * MX_BLOCK]
+            amax = float(np.max(np.abs(blk)))
+            shared = max(math.frexp(amax)[1] - 1 - 8, -127) if amax > 0 else -127
+            scales[t, b] = shared + 127
+            for i, x in enumerate(blk):
+                codes[t, b * MX_BLOCK + i] = e4m3_code(math.ldexp(float(x), -shared))
+    return codes, scales
 
 
 # ----------------------------------------------------------------------------
