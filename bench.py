@@ -8,6 +8,7 @@ workload: 32768 tokens x 896 fp32 logits, Zipf-skewed bias, rank range
 of logits) so they cannot be served from the 256 MB last-level cache.
 
 Also reported: the grouped-GEMM layout of the step's entries (us per call),
+the fused route + MXFP8 activation quantisation at decode (H = 7168),
 decode latency (us per call at 8, 16 and 64 tokens, eager and
 replayed from a HIP graph), the router GEMM + route at 64 and 4096 tokens,
 the roofline of the route kernel (timed live with HIP events on the launch
@@ -269,6 +270,25 @@ def main():
         except Exception as exc:  # graph capture is optional for the report
             decode_graph[f"T{Td}"] = f"unavailable: {type(exc).__name__}"
 
+    # fused route + MXFP8 activation quantisation at decode (H = 7168), one
+    # launch: us per call, eager and from a HIP graph
+    decode_quant, decode_quant_graph = {}, {}
+    for Td, c in decode_cases.items():
+        log(f"bench: decode route+quant T={Td}")
+        rng = np.random.default_rng(Td)
+        hb = torch.from_numpy((rng.standard_normal((Td, W.H)).astype(np.float32).view(np.uint32)
+                               >> 16).astype(np.uint16).view(np.int16)).to(dev)
+        dl = torch.from_numpy(c.logits).to(dev)
+        db = torch.from_numpy(c.bias).to(dev)
+        eo = M.local_num_experts(W.E, W.K, c.off, c.cnt) or W.E
+        qout = M.alloc_outputs(Td, W.K, eo, dev)
+        qws = torch.zeros(1 << 16, dtype=torch.uint8, device=dev)
+        qfn = (lambda dl=dl, db=db, hb=hb, c=c, qout=qout, qws=qws:
+               M.route_quant_local(dl, db, hb, c.off, c.cnt, out=qout, ws=qws))
+        qfn()
+        decode_quant[f"T{Td}"] = round(time_calls(qfn, args.decode_calls), 2)
+        decode_quant_graph[f"T{Td}"] = round(time_graph(qfn, args.decode_calls), 2)
+
     # ------------------------------------------------------------------
     # grouped-GEMM layout of the long-prefill step's entries (tile 128): us
     # per call (eager and replayed from a HIP graph) and GB/s over its
@@ -362,6 +382,8 @@ def main():
         "decode_us_per_call_hipgraph": decode_graph,
         "router_gemm_route": gemm,
         "grouped_layout_32768": grouped,
+        "decode_route_quant_mxfp8_us_per_call": decode_quant,
+        "decode_route_quant_mxfp8_us_per_call_hipgraph": decode_quant_graph,
         "roofline": {"bound": "hbm", "kernel": "route_rows_kernel",
                      "achieved": round(kern_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(frac, 4),

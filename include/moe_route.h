@@ -166,6 +166,34 @@ int moe_router_gemm_route(const uint16_t *hidden_bf16,
                           size_t workspace_bytes, void *stream);
 
 /*
+ * Fused route + activation quantisation ("[kimi-k3] Rank-local expert ids
+ * for the EP routed MoE (upstream #45544)", commit message: the fused
+ * route+quant launch for decode batches up to MAX_TOKENS, whose routed MoE
+ * runs MXFP4 expert weights). Routes exactly as moe_route_local and
+ * quantises the activations to OCP MXFP8 (the pages do not name the
+ * activation format; this is the reading taken):
+ *   hidden_bf16 [T, H] bf16 bit patterns, H a multiple of 32;
+ *   act_q [T, H] E4M3 codes: element v -> E4M3(v * 2^-shared), round to
+ *       nearest even, saturating at +-448;
+ *   act_scale [T, H/32] E8M0 codes: shared + 127 with shared =
+ *       max(floor(log2(max |v| of the 32-element block)) - 8, -127), and
+ *       -127 for a block of zeros.
+ * For T <= MOE_ROUTE_MAX_FUSED_TOKENS everything runs in ONE launch (the
+ * quantisation blocks run beside the routing blocks); above it the
+ * quantisation is one more launch before the routing. hidden_bf16 and act_q
+ * must be 16-byte aligned (else MOE_ERR_SHAPE); H not a positive multiple
+ * of 32 -> MOE_ERR_SHAPE; NULL activation pointers with T > 0 ->
+ * MOE_ERR_NULL; every routing argument is checked as by moe_route_local,
+ * all before any launch.
+ */
+int moe_route_quant_local(const float *logits, const float *bias, int32_t num_tokens,
+                          const moe_route_params *params, int32_t local_expert_offset,
+                          int32_t num_local_experts, const uint16_t *hidden_bf16,
+                          int32_t hidden, uint8_t *act_q, uint8_t *act_scale,
+                          const moe_route_outputs *out, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/*
  * Grouped-GEMM layout of a routing call's entries, the index arrays a
  * contiguous grouped GEMM over the experts consumes (an expert-parallel
  * backend builds them after routing: "Add MoonEP expert-parallel arm of the

@@ -12,6 +12,7 @@ Calls (same names as the C ABI):
     route_local(logits, bias, off, cnt, ...)       -> moe_route_local
     router_gemm_route(hidden, weight, bias, ...)   -> moe_router_gemm_route
     local_num_experts(E, K, off, cnt)              -> moe_route_local_num_experts
+    route_quant_local(logits, bias, hidden, ...)   -> moe_route_quant_local
     grouped_layout(counts, perm, tile_m, ...)      -> moe_grouped_layout
     grouped_layout_rows(n_entries, E', tile_m)     -> moe_grouped_layout_rows
     sigmoid_rn32(x, mode=0)                        -> moe_sigmoid_rn32 (diagnostic)
@@ -64,6 +65,10 @@ EXPORTS = {
     "moe_route_exact_path_tokens": (ctypes.c_int64, [_c_i32]),
     "moe_route_path_tokens": (ctypes.c_int64, [_c_i32, _c_i32]),
     "moe_grouped_layout_rows": (ctypes.c_int64, [ctypes.c_int64, _c_i32, _c_i32]),
+    "moe_route_quant_local": (ctypes.c_int, [_c_vp, _c_vp, _c_i32, ctypes.POINTER(RouteParams),
+                                             _c_i32, _c_i32, _c_vp, _c_i32, _c_vp, _c_vp,
+                                             ctypes.POINTER(RouteOutputs), _c_vp,
+                                             ctypes.c_size_t, _c_vp]),
     "moe_grouped_layout": (ctypes.c_int, [_c_vp, _c_vp, _c_i32, ctypes.c_int64, _c_i32, _c_vp,
                                           _c_vp, _c_vp, ctypes.c_int64, _c_vp]),
 }
@@ -208,6 +213,46 @@ def route_local(logits: torch.Tensor, bias: torch.Tensor, local_expert_offset: i
                                ws.data_ptr(), ws.numel(), _stream_handle(dev))
     if st:
         _check(st, "moe_route_local")
+    out["num_experts_out"] = e_out
+    return out
+
+
+def route_quant_local(logits: torch.Tensor, bias: torch.Tensor, hidden: torch.Tensor,
+                      local_expert_offset: int = 0, num_local_experts: int = 0, *,
+                      n_groups: int = 8, topk_group: int = 4, top_k: int = 16,
+                      group_topn: int = 2, out: Optional[Dict[str, torch.Tensor]] = None,
+                      ws: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """moe_route_quant_local: routing as route_local plus the MXFP8
+    activations act_q (uint8 E4M3 codes [T, H]) and act_scale (uint8 E8M0
+    codes [T, H/32]). hidden: bf16 (or 16-bit bit patterns) [T, H]."""
+    _require(logits, "logits", torch.float32, 2)
+    _require(bias, "bias", torch.float32, 1)
+    if not hidden.is_cuda or hidden.dim() != 2 or not hidden.is_contiguous() or \
+            hidden.element_size() != 2:
+        raise MoeRouteError("hidden must be a contiguous 2-d 16-bit GPU tensor")
+    T, E = logits.shape
+    H = hidden.shape[1]
+    if hidden.shape[0] != T or bias.shape[0] != E:
+        raise MoeRouteError("inconsistent shapes")
+    e_loc = local_num_experts(E, top_k, local_expert_offset, num_local_experts)
+    e_out = e_loc if e_loc > 0 else E
+    dev = logits.device
+    if out is None:
+        out = alloc_outputs(T, top_k, e_out, dev)
+    if "act_q" not in out:
+        out["act_q"] = torch.empty((T, H), dtype=torch.uint8, device=dev)
+        out["act_scale"] = torch.empty((T, H // 32), dtype=torch.uint8, device=dev)
+    if ws is None:
+        ws = workspace(dev, lib().moe_route_workspace_bytes(T, e_out, top_k))
+    prm = _params_ref(E, n_groups, topk_group, top_k, group_topn)
+    o = _outputs_struct(out)
+    st = lib().moe_route_quant_local(logits.data_ptr(), bias.data_ptr(), T, prm[1],
+                                     local_expert_offset, num_local_experts, hidden.data_ptr(),
+                                     H, out["act_q"].data_ptr(), out["act_scale"].data_ptr(),
+                                     ctypes.byref(o), ws.data_ptr(), ws.numel(),
+                                     _stream_handle(dev))
+    if st:
+        _check(st, "moe_route_quant_local")
     out["num_experts_out"] = e_out
     return out
 

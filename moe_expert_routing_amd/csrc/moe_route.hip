@@ -135,6 +135,72 @@ __device__ void block_counts(const int32_t *__restrict__ packed, int K, int e_ou
 }
 
 // ---------------------------------------------------------------------------
+// Activation quantisation of the fused route + quant launch: OCP MXFP8, E4M3
+// elements with one E8M0 scale per 32 consecutive elements of a hidden row.
+//   shared = max(floor(log2(amax)) - 8, -127)  (-127 for a block of zeros),
+//   scale code = shared + 127, element = E4M3(v * 2^-shared), round to
+//   nearest even, saturating at +-448.
+// ---------------------------------------------------------------------------
+struct QuantArgs {
+  const uint16_t *hidden;  // bf16 [T, H]; nullptr = no quantisation
+  uint8_t *q;              // E4M3 codes [T, H]
+  uint8_t *scale;          // E8M0 codes [T, H / 32]
+  int64_t nchunks;         // T * H / 8: 8-element chunks, 4 per scale block
+};
+
+constexpr int QUANT_CHUNKS_PER_BLOCK = BLOCK;  // one 16-byte chunk per thread
+
+// E4M3 code of q (binary32), round to nearest even, saturating.
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float q) {
+  const uint32_t b = __float_as_uint(q);
+  const uint32_t sg = (b >> 24) & 0x80u;
+  const uint32_t ab = b & 0x7FFFFFFFu;
+  if (ab >= 0x43E00000u) return sg | 0x7Eu;      // |q| >= 448
+  if (ab < 0x3C800000u) {                         // |q| < 2^-6: multiples of 2^-9
+    const float n = __builtin_rintf(__uint_as_float(ab) * 512.0f);  // exact product, 0..8
+    return sg | (uint32_t)n;                      // 8 is 2^-6, the code 0x08
+  }
+  const uint32_t e = (ab >> 23) - 120u;           // E4M3 biased exponent, 1..15
+  const uint32_t m = ab & 0x7FFFFFu;
+  const uint32_t r = (m + 0x7FFFFu + ((m >> 20) & 1u)) >> 20;  // 23 -> 3 bits, to even
+  const uint32_t code = (e << 3) + r;             // r = 8 carries into the exponent
+  return sg | (code > 0x7Eu ? 0x7Eu : code);
+}
+
+// Chunk c (8 elements, 16 bytes) per thread; the 4 lanes of a scale block
+// are adjacent (chunk indices 4k..4k+3 fall in lanes 4k'..4k'+3 of a wave
+// because every block starts at a multiple of 4 chunks and a wave's chunks
+// are consecutive).
+__device__ __forceinline__ void mx_quant_chunk(const QuantArgs &qa, int64_t c) {
+  const bool valid = c < qa.nchunks;
+  uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+  if (valid) raw = reinterpret_cast<const uint4 *>(qa.hidden)[c];
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  uint32_t amax = 0u;  // largest |bf16| bit pattern of the lane
+#pragma unroll
+  for (int i = 0; i < 4; ++i) amax = umax(amax, umax(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+  amax = umax(amax, dpp<DPP_XOR1>(amax));
+  amax = umax(amax, dpp<DPP_XOR2>(amax));
+  const int ef = (int)(amax >> 7);  // bf16 exponent field of the block maximum
+  const int shared = (amax == 0u || ef == 0) ? -127 : max(ef - 135, -127);
+  if (!valid) return;
+  uint32_t out[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t h = (w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+    const float v = __builtin_amdgcn_ldexpf(__uint_as_float(h << 16), -shared);
+    out[i >> 2] |= e4m3_rne_sat(v) << (8 * (i & 3));
+  }
+  reinterpret_cast<uint2 *>(qa.q)[c] = make_uint2(out[0], out[1]);
+  if ((c & 3) == 0) qa.scale[c >> 2] = (uint8_t)(shared + 127);
+}
+
+// Standalone quantisation (the prefill path of the fused entry point).
+__global__ __launch_bounds__(BLOCK) void mx_quant_kernel(QuantArgs qa) {
+  mx_quant_chunk(qa, (int64_t)blockIdx.x * QUANT_CHUNKS_PER_BLOCK + threadIdx.x);
+}
+
+// ---------------------------------------------------------------------------
 // Decode path: one launch for T <= 64.
 // ---------------------------------------------------------------------------
 template <int NP, int LPG>
@@ -142,7 +208,13 @@ __global__ __launch_bounds__(BLOCK) void route_decode_kernel(
     const float *__restrict__ logits, const float *__restrict__ bias, int T, RouteParams p,
     int32_t *__restrict__ ids, float *__restrict__ wts, int32_t *__restrict__ packed,
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
-    int32_t *__restrict__ inv, uint32_t *__restrict__ ticket) {
+    int32_t *__restrict__ inv, uint32_t *__restrict__ ticket, QuantArgs qa) {
+  // blocks past the routing blocks quantise the activations (no ticket)
+  const int nroute = T > 0 ? (T + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK : 1;
+  if ((int)blockIdx.x >= nroute) {
+    mx_quant_chunk(qa, (int64_t)(blockIdx.x - nroute) * QUANT_CHUNKS_PER_BLOCK + threadIdx.x);
+    return;
+  }
   __shared__ unsigned long long mask[MOE_ROUTE_MAX_EXPERTS];
   __shared__ int32_t offs[MOE_ROUTE_MAX_EXPERTS + 1];
   __shared__ int32_t wave_tot[WAVES_PER_BLOCK];
@@ -161,7 +233,7 @@ __global__ __launch_bounds__(BLOCK) void route_decode_kernel(
   // Publish this block's outputs, then take a ticket.
   __threadfence();
   __syncthreads();
-  if (threadIdx.x == 0) is_last = (atomicAdd(ticket, 1u) == gridDim.x - 1u);
+  if (threadIdx.x == 0) is_last = (atomicAdd(ticket, 1u) == (uint32_t)nroute - 1u);
   __syncthreads();
   if (!is_last) return;
   __threadfence();
@@ -515,15 +587,20 @@ static bool rows_path_applies(const RouteParams &rp, const float *logits) {
 
 template <int NP, int LPG>
 static hipError_t launch_route(const float *logits, const float *bias, int T, const RouteParams &rp,
-                               const moe_route_outputs *o, char *ws, hipStream_t st) {
+                               const moe_route_outputs *o, char *ws, hipStream_t st,
+                               const QuantArgs &qa) {
+  const int qblocks =
+      qa.hidden ? (int)((qa.nchunks + QUANT_CHUNKS_PER_BLOCK - 1) / QUANT_CHUNKS_PER_BLOCK) : 0;
   if (T <= MOE_ROUTE_MAX_FUSED_TOKENS) {
-    const int grid = T > 0 ? (T + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK : 1;
+    // one launch: routing blocks, then the quantisation blocks
+    const int grid = (T > 0 ? (T + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK : 1) + qblocks;
     hipExtLaunchKernelGGL(route_decode_kernel<NP, LPG>, dim3(grid), dim3(BLOCK), 0, st,
                           g_ev_before, g_ev_after, 0, logits, bias, T, rp, o->topk_ids,
                           o->topk_weights, o->packed, o->counts, o->offsets, o->perm,
-                          o->inv_perm, reinterpret_cast<uint32_t *>(ws));
+                          o->inv_perm, reinterpret_cast<uint32_t *>(ws), qa);
     return hipGetLastError();
   }
+  if (qblocks > 0) mx_quant_kernel<<<qblocks, BLOCK, 0, st>>>(qa);
   const bool rows_path = LPG == 8 && NP == 7 && rows_path_applies(rp, logits);
   const int tpb = rows_path ? ROWS_TOKENS_PER_BLOCK : WAVES_PER_BLOCK;
   const int nblk = (T + tpb - 1) / tpb;
@@ -575,7 +652,7 @@ int validate_route_call(const float *logits, const float *bias, int32_t T,
 static int route_impl(const float *logits, const float *bias, int32_t T,
                       const moe_route_params *prm, int32_t off, int32_t cnt,
                       const moe_route_outputs *o, void *workspace, size_t ws_bytes,
-                      void *stream) {
+                      void *stream, const QuantArgs &qa = QuantArgs{nullptr, nullptr, nullptr, 0}) {
   int e_out = 0;
   const int st = validate_route_call(logits, bias, T, prm, off, cnt, o, workspace, ws_bytes,
                                      &e_out);
@@ -599,18 +676,18 @@ static int route_impl(const float *logits, const float *bias, int32_t T,
   hipError_t err;
   // the 896-expert, 8-group shape gets constant lanes per group
   if (rp.E == 896 && rp.lpg == 8) {
-    err = launch_route<7, 8>(logits, bias, T, rp, o, ws, s);
+    err = launch_route<7, 8>(logits, bias, T, rp, o, ws, s, qa);
     return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
   }
   switch (rp.E / 128) {
-    case 1: err = launch_route<1, 0>(logits, bias, T, rp, o, ws, s); break;
-    case 2: err = launch_route<2, 0>(logits, bias, T, rp, o, ws, s); break;
-    case 3: err = launch_route<3, 0>(logits, bias, T, rp, o, ws, s); break;
-    case 4: err = launch_route<4, 0>(logits, bias, T, rp, o, ws, s); break;
-    case 5: err = launch_route<5, 0>(logits, bias, T, rp, o, ws, s); break;
-    case 6: err = launch_route<6, 0>(logits, bias, T, rp, o, ws, s); break;
-    case 7: err = launch_route<7, 0>(logits, bias, T, rp, o, ws, s); break;
-    case 8: err = launch_route<8, 0>(logits, bias, T, rp, o, ws, s); break;
+    case 1: err = launch_route<1, 0>(logits, bias, T, rp, o, ws, s, qa); break;
+    case 2: err = launch_route<2, 0>(logits, bias, T, rp, o, ws, s, qa); break;
+    case 3: err = launch_route<3, 0>(logits, bias, T, rp, o, ws, s, qa); break;
+    case 4: err = launch_route<4, 0>(logits, bias, T, rp, o, ws, s, qa); break;
+    case 5: err = launch_route<5, 0>(logits, bias, T, rp, o, ws, s, qa); break;
+    case 6: err = launch_route<6, 0>(logits, bias, T, rp, o, ws, s, qa); break;
+    case 7: err = launch_route<7, 0>(logits, bias, T, rp, o, ws, s, qa); break;
+    case 8: err = launch_route<8, 0>(logits, bias, T, rp, o, ws, s, qa); break;
     default: return MOE_ERR_UNSUPPORTED;
   }
   return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
@@ -663,6 +740,23 @@ int moe_route_local(const float *logits, const float *bias, int32_t num_tokens,
                     size_t workspace_bytes, void *stream) {
   return moe::route_impl(logits, bias, num_tokens, params, local_expert_offset,
                          num_local_experts, out, workspace, workspace_bytes, stream);
+}
+
+int moe_route_quant_local(const float *logits, const float *bias, int32_t num_tokens,
+                          const moe_route_params *params, int32_t local_expert_offset,
+                          int32_t num_local_experts, const uint16_t *hidden_bf16,
+                          int32_t hidden, uint8_t *act_q, uint8_t *act_scale,
+                          const moe_route_outputs *out, void *workspace, size_t workspace_bytes,
+                          void *stream) {
+  if (hidden <= 0 || hidden % 32 != 0) return MOE_ERR_SHAPE;
+  if (num_tokens > 0 && (!hidden_bf16 || !act_q || !act_scale)) return MOE_ERR_NULL;
+  if (((uintptr_t)hidden_bf16 | (uintptr_t)act_q) % 16 != 0) return MOE_ERR_SHAPE;
+  const int64_t nchunks = (int64_t)(num_tokens > 0 ? num_tokens : 0) * hidden / 8;
+  if ((nchunks + moe::QUANT_CHUNKS_PER_BLOCK - 1) / moe::QUANT_CHUNKS_PER_BLOCK > INT32_MAX / 2)
+    return MOE_ERR_SHAPE;
+  const moe::QuantArgs qa{num_tokens > 0 ? hidden_bf16 : nullptr, act_q, act_scale, nchunks};
+  return moe::route_impl(logits, bias, num_tokens, params, local_expert_offset,
+                         num_local_experts, out, workspace, workspace_bytes, stream, qa);
 }
 
 int64_t moe_route_exact_path_tokens(int32_t reset) {

@@ -135,6 +135,24 @@ def test_router_gemm_validation(L):
     assert call(logits=FAKE + 8) == ERR_SHAPE   # logits 16-byte aligned
 
 
+def test_route_quant_validation(L):
+    prm = _params()
+    o = _outs()
+    def call(T=8, hidden=FAKE, H=7168, q=FAKE, sc=FAKE, off=0, cnt=0, p=prm, ws_bytes=1 << 20):
+        return L.moe_route_quant_local(FAKE, FAKE, T, ctypes.byref(p), off, cnt, hidden, H, q, sc,
+                                       ctypes.byref(o), FAKE, ws_bytes, None)
+    assert call(H=7160) == ERR_SHAPE         # not a multiple of 32
+    assert call(H=0) == ERR_SHAPE
+    assert call(hidden=None) == ERR_NULL
+    assert call(q=None) == ERR_NULL
+    assert call(sc=None) == ERR_NULL
+    assert call(hidden=FAKE + 8) == ERR_SHAPE  # 16-byte alignment
+    assert call(q=FAKE + 4) == ERR_SHAPE
+    assert call(p=_params(N=3)) == ERR_UNSUP   # routing arguments checked as by moe_route_local
+    assert call(off=890, cnt=10) == ERR_RANGE
+    assert call(ws_bytes=16) == ERR_WS
+
+
 def test_grouped_layout_validation(L):
     assert L.moe_grouped_layout_rows(100, 128, 64) == 100 + 128 * 63
     assert L.moe_grouped_layout_rows(0, 896, 1) == 0
