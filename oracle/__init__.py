@@ -16,6 +16,7 @@ from .route_ref import (  # noqa: F401
     e4m3_code,
     e4m3_value,
     mxfp8_quantize,
+    balance_plan,
     group_scores,
     kept_groups,
     local_num_experts,

@@ -41,7 +41,9 @@ rounding and the renormalisation. This oracle takes the plainest readings:
 * grouped-GEMM layout (a consumer of counts and perm): each id's entries in
   permutation order from its tile-padded offset, padding rows marked -1;
 * activations of the fused route + quant launch: OCP MXFP8 (E4M3 elements,
-  one E8M0 scale per 32 elements), round to nearest even, saturating.
+  one E8M0 scale per 32 elements), round to nearest even, saturating;
+* a static balancing plan over N expert-owning ranks: owners keep up to
+  their share of the entries, the surplus fills the short ranks in order.
 
 Every function below has a pin in ``tests/test_oracle_*.py`` (brute force,
 library routines, closed forms, mpmath, and the value the pages print).
@@ -296,6 +298,57 @@ def grouped_layout(counts: np.ndarray, perm: np.ndarray, tile_m: int,
             row_entry[r] = int(perm[p + j])
         p += counts[e]
     return padded.astype(np.int32), m_indices.astype(np.int32), row_entry.astype(np.int32)
+
+
+# ----------------------------------------------------------------------------
+# Static per-rank balancing plan
+# ----------------------------------------------------------------------------
+# The pages give only the goal: the expert-parallel dispatch holds every
+# rank at exactly S*K routed entries by reassigning the surplus of
+# overloaded expert owners ("Add MoonEP expert-parallel arm of the Kimi-K3
+# B300 agentic sweep", PR description: what MoonEP does). The plan taken
+# here, over the expert-major order of one routing call with global ids
+# (experts owned in contiguous ranges of E / N by ranks 0..N-1):
+#   target[r] = n // N (+1 for the first n % N ranks), n = T*K entries;
+#   rank r keeps the first min(load[r], target[r]) of its own entries;
+#   the rest of every overloaded rank, in rank order, is the surplus
+#   sequence; the ranks short of their target take consecutive runs of it,
+#   in rank order, until each holds exactly its target.
+# No plan can move fewer entries (every overloaded rank must lose its
+# excess), and the order inside each expert is kept.
+
+
+def balance_plan(counts: np.ndarray, n_ranks: int) -> Tuple[np.ndarray, np.ndarray]:
+    """dest[p]: rank of the p-th entry in expert-major order; rank_counts
+    [n_ranks, E]: entries of expert e each rank processes."""
+    counts = [int(c) for c in counts]
+    E = len(counts)
+    per = E // n_ranks
+    n = sum(counts)
+    target = [n // n_ranks + (1 if r < n % n_ranks else 0) for r in range(n_ranks)]
+    load = [sum(counts[r * per:(r + 1) * per]) for r in range(n_ranks)]
+    keep = [min(load[r], target[r]) for r in range(n_ranks)]
+    deficit = [target[r] - keep[r] for r in range(n_ranks)]
+    # ranks short of their target, one slot per missing entry, in rank order
+    takers = [r for r in range(n_ranks) for _ in range(deficit[r])]
+    dest = np.zeros(n, dtype=np.int64)
+    rank_counts = np.zeros((n_ranks, E), dtype=np.int64)
+    p = 0            # position in expert-major order
+    moved = 0        # entries of the surplus sequence assigned so far
+    for r in range(n_ranks):
+        own = 0      # entries of rank r seen so far
+        for e in range(r * per, (r + 1) * per):
+            for _ in range(counts[e]):
+                if own < keep[r]:
+                    d = r
+                else:
+                    d = takers[moved]
+                    moved += 1
+                dest[p] = d
+                rank_counts[d, e] += 1
+                own += 1
+                p += 1
+    return dest.astype(np.int32), rank_counts.astype(np.int32)
 
 
 # ----------------------------------------------------------------------------
