@@ -8,6 +8,7 @@ workload: 32768 tokens x 896 fp32 logits, Zipf-skewed bias, rank range
 of logits) so they cannot be served from the 256 MB last-level cache.
 
 Also reported: the grouped-GEMM layout of the step's entries (us per call),
+a static balancing plan over 8 expert-owning ranks (us per call),
 the fused route + MXFP8 activation quantisation at decode (H = 7168),
 decode latency (us per call at 8, 16 and 64 tokens, eager and
 replayed from a HIP graph), the router GEMM + route at 64 and 4096 tokens,
@@ -311,6 +312,23 @@ def main():
                                   "us_per_call_hipgraph": round(gl_graph_us, 2), "rows": rows,
                                   "gbps_hipgraph": round(gl_bytes / (gl_graph_us * 1e-6) / 1e9, 1)}
 
+    # static balancing plan over 8 expert-owning ranks from the global counts
+    # of the long-prefill input (routed once with global ids, untimed)
+    log("bench: balancing plan")
+    gout = M.route(lg[0], bs[0])
+    n_ent = T * W.K
+    plan = M.balance_plan(gout["counts"], 8, n_ent)
+    pl_fn = lambda: M.balance_plan(gout["counts"], 8, n_ent, out=plan)
+    pl_fn()
+    torch.cuda.synchronize()
+    rc = plan["rank_counts"].cpu().numpy()
+    per = W.E // 8
+    own = sum(int(rc[r, r * per:(r + 1) * per].sum()) for r in range(8))
+    balance = {"ranks": 8, "entries": n_ent, "moved_entries": n_ent - own,
+               "us_per_call": round(time_calls(pl_fn, 200), 2),
+               "us_per_call_hipgraph": round(time_graph(pl_fn, 200), 2)}
+    del gout
+
     # ------------------------------------------------------------------
     # router GEMM + route
     # ------------------------------------------------------------------
@@ -382,6 +400,7 @@ def main():
         "decode_us_per_call_hipgraph": decode_graph,
         "router_gemm_route": gemm,
         "grouped_layout_32768": grouped,
+        "balance_plan_32768": balance,
         "decode_route_quant_mxfp8_us_per_call": decode_quant,
         "decode_route_quant_mxfp8_us_per_call_hipgraph": decode_quant_graph,
         "roofline": {"bound": "hbm", "kernel": "route_rows_kernel",

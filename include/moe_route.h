@@ -225,6 +225,31 @@ int moe_grouped_layout(const int32_t *counts, const int32_t *perm, int32_t num_e
                        int32_t *m_indices, int32_t *row_entry, int64_t rows, void *stream);
 
 /*
+ * Static per-rank balancing plan for an expert-parallel dispatch that holds
+ * every rank at the same number of routed entries by moving the surplus of
+ * overloaded expert owners ("Add MoonEP expert-parallel arm of the Kimi-K3
+ * B300 agentic sweep", PR description; the pages give the goal, this is the
+ * plan taken). From counts [E] of one routing call with GLOBAL ids (n_entries
+ * = T*K, counts summing to it) and n_ranks ranks owning the experts in
+ * contiguous ranges of E / n_ranks:
+ *   target[r] = n_entries / n_ranks, +1 for the first n_entries % n_ranks;
+ *   rank r keeps the first min(load[r], target[r]) of its own entries in
+ *   expert-major order (the order of perm); the remaining entries of every
+ *   overloaded rank, in rank order, are handed out in consecutive runs to the
+ *   ranks below target, in rank order, until each holds its target.
+ *   dest [n_entries]: the rank that processes the p-th entry of perm;
+ *   rank_counts [n_ranks][E]: entries of expert e processed on rank r.
+ * Device pointers owned by the caller; asynchronous on stream; nothing
+ * allocated. Checked on the host before any launch: 1 <= n_ranks <= 64,
+ * 1 <= E <= 1024 with E % n_ranks == 0, 0 <= n_entries <=
+ * MOE_GROUPED_MAX_ENTRIES (else MOE_ERR_SHAPE); NULL counts / rank_counts,
+ * or NULL dest with n_entries > 0 -> MOE_ERR_NULL. Counts that do not sum
+ * to n_entries give a wrong plan but no access outside the arrays.
+ */
+int moe_balance_plan(const int32_t *counts, int32_t num_experts, int32_t n_ranks,
+                     int64_t n_entries, int32_t *dest, int32_t *rank_counts, void *stream);
+
+/*
  * Diagnostic: y[i] = the binary32 nearest to 1 / (1 + e^-x[i]) for n
  * elements, with the routing kernels' own sigmoid. mode 0 = the production
  * evaluation; mode 1 = the double-double re-evaluation only (the path taken

@@ -14,6 +14,7 @@ Calls (same names as the C ABI):
     local_num_experts(E, K, off, cnt)              -> moe_route_local_num_experts
     route_quant_local(logits, bias, hidden, ...)   -> moe_route_quant_local
     grouped_layout(counts, perm, tile_m, ...)      -> moe_grouped_layout
+    balance_plan(counts, n_ranks, n_entries)       -> moe_balance_plan
     grouped_layout_rows(n_entries, E', tile_m)     -> moe_grouped_layout_rows
     sigmoid_rn32(x, mode=0)                        -> moe_sigmoid_rn32 (diagnostic)
 """
@@ -65,6 +66,8 @@ EXPORTS = {
     "moe_route_exact_path_tokens": (ctypes.c_int64, [_c_i32]),
     "moe_route_path_tokens": (ctypes.c_int64, [_c_i32, _c_i32]),
     "moe_grouped_layout_rows": (ctypes.c_int64, [ctypes.c_int64, _c_i32, _c_i32]),
+    "moe_balance_plan": (ctypes.c_int, [_c_vp, _c_i32, _c_i32, ctypes.c_int64, _c_vp, _c_vp,
+                                        _c_vp]),
     "moe_route_quant_local": (ctypes.c_int, [_c_vp, _c_vp, _c_i32, ctypes.POINTER(RouteParams),
                                              _c_i32, _c_i32, _c_vp, _c_i32, _c_vp, _c_vp,
                                              ctypes.POINTER(RouteOutputs), _c_vp,
@@ -377,6 +380,24 @@ def grouped_layout(counts: torch.Tensor, perm: torch.Tensor, tile_m: int, *,
                                   _stream_handle(dev))
     if st:
         _check(st, "moe_grouped_layout")
+    return out
+
+
+def balance_plan(counts: torch.Tensor, n_ranks: int, n_entries: int, *,
+                 out: Optional[Dict[str, torch.Tensor]] = None) -> Dict[str, torch.Tensor]:
+    """moe_balance_plan over a routing call's global counts [E]: dest
+    [n_entries] (rank of each entry of perm) and rank_counts [n_ranks, E]."""
+    _require(counts, "counts", torch.int32, 1)
+    E = counts.shape[0]
+    dev = counts.device
+    if out is None:
+        out = {"dest": torch.empty(n_entries, dtype=torch.int32, device=dev),
+               "rank_counts": torch.empty((n_ranks, E), dtype=torch.int32, device=dev)}
+    st = lib().moe_balance_plan(counts.data_ptr(), E, n_ranks, n_entries,
+                                out["dest"].data_ptr() if n_entries else None,
+                                out["rank_counts"].data_ptr(), _stream_handle(dev))
+    if st:
+        _check(st, "moe_balance_plan")
     return out
 
 

@@ -530,6 +530,106 @@ __global__ __launch_bounds__(BLOCK) void grouped_layout_kernel(
   }
 }
 
+// Static per-rank balancing plan over N ranks that own the experts in
+// contiguous ranges of E / N, from one routing call's global counts: rank r
+// keeps the first min(load[r], target[r]) of its own entries (expert-major
+// order), the rest of every overloaded rank forms one surplus sequence in
+// rank order, and the ranks short of their target take consecutive runs of
+// it in rank order; target[r] = n / N, +1 for the first n % N ranks. Every
+// block forms the scans in LDS; each thread writes 4 consecutive entries'
+// ranks; block 0 writes rank_counts [N][E] from interval overlaps.
+constexpr int PLAN_MAX_RANKS = 64;
+constexpr int PLAN_PER_THREAD = 4;  // the int4 stores below assume 4
+
+__global__ __launch_bounds__(BLOCK) void balance_plan_kernel(const int32_t *__restrict__ counts,
+                                                             int E, int n_ranks, int64_t n,
+                                                             int32_t *__restrict__ dest,
+                                                             int32_t *__restrict__ rank_counts) {
+  __shared__ int32_t offs[MOE_ROUTE_MAX_EXPERTS + 1];
+  __shared__ int32_t wave_tot[WAVES_PER_BLOCK];
+  __shared__ int32_t A[PLAN_MAX_RANKS + 1], keep[PLAN_MAX_RANKS];
+  __shared__ int32_t SP[PLAN_MAX_RANKS + 1], DP[PLAN_MAX_RANKS + 1];
+  int cv[4];
+  scan_load(counts, E, cv);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) cv[k] = max(cv[k], 0);
+  scan_store(cv, E, offs, wave_tot);
+  const int per = E / n_ranks;
+  if (threadIdx.x < 64) {  // one wave: per-rank keep, surplus and deficit, scanned
+    const int r = threadIdx.x;
+    int kp = 0, sur = 0, def = 0;
+    if (r < n_ranks) {
+      const int a = offs[r * per];
+      const int load = offs[(r + 1) * per] - a;
+      const int tgt = (int)(n / n_ranks) + (r < (int)(n % n_ranks) ? 1 : 0);
+      kp = min(load, tgt);
+      sur = load - kp;
+      def = tgt - kp;
+      A[r] = a;
+      keep[r] = kp;
+    }
+    const int si = wave_inclusive_scan(sur), di = wave_inclusive_scan(def);
+    if (r < n_ranks) {
+      SP[r + 1] = si;
+      DP[r + 1] = di;
+    }
+    if (r == 0) {
+      SP[0] = 0;
+      DP[0] = 0;
+      A[n_ranks] = offs[E];
+    }
+  }
+  lds_barrier();
+  if (blockIdx.x == 0) {
+    for (int e = threadIdx.x; e < E; e += BLOCK) {
+      const int r = e / per;
+      const int a = offs[e] - A[r], b = offs[e + 1] - A[r];  // e's entries among rank r's
+      const int kept = max(min(b, keep[r]) - a, 0);
+      const int s0 = SP[r] + max(a, keep[r]) - keep[r], s1 = SP[r] + b - keep[r];
+      for (int q = 0; q < n_ranks; ++q) {
+        int c = max(min(s1, DP[q + 1]) - max(s0, DP[q]), 0);  // surplus run taken by q
+        if (q == r) c += kept;
+        rank_counts[(size_t)q * E + e] = c;
+      }
+    }
+  }
+  const int64_t p0 = ((int64_t)blockIdx.x * BLOCK + threadIdx.x) * PLAN_PER_THREAD;
+  if (p0 >= n) return;
+  int d[PLAN_PER_THREAD];
+#pragma unroll
+  for (int k = 0; k < PLAN_PER_THREAD; ++k) {
+    const int64_t p = p0 + k;
+    // the owner: the largest r with A[r] <= p (ranks without entries skipped)
+    int lo = 0, hi = n_ranks + 1;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if ((int64_t)A[mid] <= p) lo = mid;
+      else hi = mid;
+    }
+    const int r = min(lo, n_ranks - 1);
+    const int own = (int)(p - A[r]);
+    if (own < keep[r]) {
+      d[k] = r;
+    } else {
+      const int sidx = SP[r] + own - keep[r];  // index in the surplus sequence
+      int l2 = 0, h2 = n_ranks + 1;
+      while (h2 - l2 > 1) {
+        const int mid = (l2 + h2) >> 1;
+        if (DP[mid] <= sidx) l2 = mid;
+        else h2 = mid;
+      }
+      d[k] = min(l2, n_ranks - 1);
+    }
+  }
+  if (p0 + PLAN_PER_THREAD <= n && ((uintptr_t)(dest + p0) & 15) == 0) {
+    *reinterpret_cast<int4 *>(dest + p0) = make_int4(d[0], d[1], d[2], d[3]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < PLAN_PER_THREAD; ++k)
+      if (p0 + k < n) dest[p0 + k] = d[k];
+  }
+}
+
 // Diagnostic sigmoid kernel.
 __global__ void sigmoid_kernel(const float *__restrict__ x, float *__restrict__ y, int64_t n,
                                int mode) {
@@ -818,6 +918,21 @@ int moe_grouped_layout(const int32_t *counts, const int32_t *perm, int32_t num_e
   moe::grouped_layout_kernel<<<(int)grid, moe::BLOCK, 0, st>>>(
       counts, perm, num_experts_out, n_entries, tile_m, padded_offsets, m_indices, row_entry,
       rows);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_balance_plan(const int32_t *counts, int32_t num_experts, int32_t n_ranks,
+                     int64_t n_entries, int32_t *dest, int32_t *rank_counts, void *stream) {
+  if (n_ranks < 1 || n_ranks > moe::PLAN_MAX_RANKS) return MOE_ERR_SHAPE;
+  if (num_experts < 1 || num_experts > MOE_ROUTE_MAX_EXPERTS || num_experts % n_ranks != 0)
+    return MOE_ERR_SHAPE;
+  if (n_entries < 0 || n_entries > MOE_GROUPED_MAX_ENTRIES) return MOE_ERR_SHAPE;
+  if (!counts || !rank_counts || (n_entries > 0 && !dest)) return MOE_ERR_NULL;
+  const int64_t per_block = (int64_t)moe::BLOCK * moe::PLAN_PER_THREAD;
+  const int64_t grid = n_entries > 0 ? (n_entries + per_block - 1) / per_block : 1;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  moe::balance_plan_kernel<<<(int)grid, moe::BLOCK, 0, st>>>(counts, num_experts, n_ranks,
+                                                             n_entries, dest, rank_counts);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

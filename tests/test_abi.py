@@ -153,6 +153,19 @@ def test_route_quant_validation(L):
     assert call(ws_bytes=16) == ERR_WS
 
 
+def test_balance_plan_validation(L):
+    def call(counts=FAKE, E=896, N=8, n=128, dest=FAKE, rc=FAKE):
+        return L.moe_balance_plan(counts, E, N, n, dest, rc, None)
+    assert call(N=0) == ERR_SHAPE
+    assert call(N=65) == ERR_SHAPE
+    assert call(E=900) == ERR_SHAPE          # not a multiple of the rank count
+    assert call(E=2048, N=8) == ERR_SHAPE    # above 1024 experts
+    assert call(n=-1) == ERR_SHAPE
+    assert call(counts=None) == ERR_NULL
+    assert call(rc=None) == ERR_NULL
+    assert call(dest=None) == ERR_NULL
+
+
 def test_grouped_layout_validation(L):
     assert L.moe_grouped_layout_rows(100, 128, 64) == 100 + 128 * 63
     assert L.moe_grouped_layout_rows(0, 896, 1) == 0
