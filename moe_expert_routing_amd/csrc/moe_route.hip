@@ -365,8 +365,7 @@ __global__ __launch_bounds__(ROWS_BLOCK, 8) void route_rows_kernel(
       float b[14], x[14];
       load_lane_layout<7, 8>(row, p, lane, x);
       load_lane_layout<7, 8>(bias, p, lane, b);
-      route_token<7, 8>(row, x, b, bias, p, lane, t, &lds.wave[wave].w, ids, wts, packed,
-                        /*fast_first=*/false);
+      route_token_plain<7, 8>(row, x, b, p, lane, t, ids, wts, packed);
     }
   }
   block_counts<ROWS_BLOCK>(packed, p.K, p.e_out, tb,

@@ -486,8 +486,15 @@ __device__ __forceinline__ uint32_t route_rows4(const float *__restrict__ logits
   const int K = p.K;
 
   // ---- streaming, groups, merged pool, extraction -----------------------------
+  // Issue priority by phase (s_setprio; measured about 1 us faster at 32K
+  // tokens): waves still streaming their rows go first, so every row's loads
+  // are in flight early; the selection runs at 1, the stores at 0; a wave
+  // that must refine a row goes first again, so that its extra work does not
+  // trail the rest of the grid.
   uint32_t a[PP], b[PP];
+  __builtin_amdgcn_s_setprio(3);
   stream_pools(row, bias_lds, c, sub, a, b);
+  __builtin_amdgcn_s_setprio(1);
   bool kept_a, kept_b;
   const bool groups_ok = approx_groups(a, b, p, c, kept_a, kept_b);  // row-uniform
   bool fail = !groups_ok;
@@ -545,6 +552,7 @@ __device__ __forceinline__ uint32_t route_rows4(const float *__restrict__ logits
   }
   const uint32_t row_fail = pre_fail | ((valid && !boundary_ok && pre_fail == 0u) ? 1u : 0u);
 
+  __builtin_amdgcn_s_setprio(0);
   // ---- epilogue: lane u takes slot u (the winner of exact rank u) ----------------
   if (row_fail == 0u && act) L->slot[r][rank] = make_uint2((uint32_t)my_id, __float_as_uint(my_s));
   wave_lds_sync();
@@ -557,6 +565,7 @@ __device__ __forceinline__ uint32_t route_rows4(const float *__restrict__ logits
   bool done = row_fail == 0u;
   const bool need = !done && valid;
   if (__ballot(need)) {
+    __builtin_amdgcn_s_setprio(3);
     wave_lds_sync();
     done = refine_rows(row, bias_g, a, b, need, groups_ok, kept_a, kept_b, M, p, r, u, t, L, ids,
                        wts, packed) ||

@@ -185,7 +185,7 @@ __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > 
 // Approximate scores
 // ---------------------------------------------------------------------------
 // Bound on |fast_sigmoid(x) - RN32(sigma(x))| over all finite binary32 x.
-constexpr float FAST_SIG_ERR = 0x1p-20f;
+constexpr float FAST_SIG_ERR = 0x1p-22f;
 
 __device__ __forceinline__ float fast_sigmoid(float x) {
   const float e = __builtin_amdgcn_exp2f(x * -1.44269504088896340736f);
@@ -677,6 +677,26 @@ __device__ __forceinline__ int route_token(const float *__restrict__ row,
     if (!select_token<NP, LPG, true>(row, bias_g, x, bias, p, ln, L, my_id, my_s))
       route_token_exact<NP, LPG>(row, x, bias, p, ln, my_id, my_s);
   }
+  return route_epilogue(my_id, my_s, p, ln, t, ids, wts, packed);
+}
+
+// Routes token t with the plain exact pipeline only (exact scores, exact
+// group scores, top_k by wave argmax): the fallback of the four-tokens-per-
+// wave path, kept small so that it costs that path few registers.
+template <int NP, int LPG>
+__device__ __forceinline__ int route_token_plain(const float *__restrict__ row,
+                                                 const float (&x)[2 * NP],
+                                                 const float (&bias)[2 * NP],
+                                                 const RouteParams &p, int lane, int64_t t,
+                                                 int32_t *__restrict__ ids,
+                                                 float *__restrict__ wts,
+                                                 int32_t *__restrict__ packed) {
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  int my_id = 0;
+  float my_s = 0.0f;
+  if (ln == 0) atomicAdd(&g_exact_path_tokens, 1ull);
+  route_token_exact<NP, LPG>(row, x, bias, p, ln, my_id, my_s);
   return route_epilogue(my_id, my_s, p, ln, t, ids, wts, packed);
 }
 
