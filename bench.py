@@ -25,6 +25,7 @@ import hashlib
 import json
 import os
 import platform
+import re
 import statistics
 import sys
 import time
@@ -59,11 +60,17 @@ def parse():
 
 
 def source_digest() -> str:
+    """Digest of the routing sources' code: comments and blank space are
+    dropped first, so that a documentation edit does not retire a profile
+    taken on the same kernels."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "moe_expert_routing_amd", "csrc")
     for name in ROUTE_SOURCES:
-        with open(os.path.join(csrc, name), "rb") as fh:
-            h.update(name.encode() + fh.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(name.encode() + " ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
@@ -186,13 +193,14 @@ def main():
     log(f"bench: {ms_per_step * 1e3:.1f} us/step, route kernel {kern_avg_ms * 1e3:.1f} us")
 
     # which kernel path the tokens of one step took
-    for path in (M.PATH_EXACT, M.PATH_REFINED, M.PATH_REROUTED):
+    for path in (M.PATH_EXACT, M.PATH_REFINED, M.PATH_REROUTED, M.PATH_RESCORED):
         M.path_tokens(path, reset=True)
     step(0)
     torch.cuda.synchronize()
     paths = {"tokens": T, "exact_refinement": M.path_tokens(M.PATH_REFINED, reset=True),
              "rerouted_one_token_per_wave": M.path_tokens(M.PATH_REROUTED, reset=True),
-             "exact_pipeline": M.path_tokens(M.PATH_EXACT, reset=True)}
+             "exact_pipeline": M.path_tokens(M.PATH_EXACT, reset=True),
+             "rescored_one_token_per_wave": M.path_tokens(M.PATH_RESCORED, reset=True)}
 
     # ------------------------------------------------------------------
     # plain device copy of 512 MiB (HBM reference bandwidth; the same copy

@@ -4,7 +4,8 @@
 //  * decode, T <= 64: ONE launch. Blocks of 4 waves route one token per wave
 //    and publish their outputs; the last block to arrive (ticket in the
 //    workspace control block) builds counts, offsets and the permutation from
-//    per-expert 64-bit token masks in LDS.
+//    per-expert 64-bit token masks in LDS. With moe_route_quant_local, more
+//    blocks of the same launch quantise the activations to MXFP8.
 //  * prefill, T > 64: three launches.
 //      route:   four tokens per wave (896 experts in 8 groups, route_rows.hpp)
 //               or one token per wave (other shapes); at the end of every
@@ -14,6 +15,9 @@
 //               total -> counts[e'].
 //      scatter: offsets = exclusive scan of counts; each entry goes to
 //               offsets[e'] + hist[e'][blk] + rank8[f].
+// Consumers of one call's counts and perm, one launch each: the grouped-GEMM
+// layout (moe_grouped_layout) and the static balancing plan over expert-
+// owning ranks (moe_balance_plan).
 // Within one token the output ids are distinct (top-k ids are distinct and
 // the relabelled ids are unique per row), so "ascending flat index within an
 // expert" is "ascending token", and a token's position among the entries of
