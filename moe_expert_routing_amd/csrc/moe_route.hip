@@ -64,12 +64,22 @@ __device__ __forceinline__ void lds_barrier() {
 // total, in two steps so that a caller can issue other loads between them:
 // scan_load reads this thread's 4 inputs; scan_store scans and writes.
 // All BLOCK threads must call both.
+// The loads take clamped indices and are unconditional, so all four are in
+// flight together (a guarded load becomes a branch that waits on its own).
 __device__ __forceinline__ void scan_load(const int32_t *in, int n, int (&v)[4]) {
+  if (n <= 0) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = 0;
+    return;
+  }
+  int x[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int idx = threadIdx.x * 4 + k;
-    v[k] = idx < n ? in[idx] : 0;
+    x[k] = in[idx < n ? idx : n - 1];
   }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) v[k] = ((int)threadIdx.x * 4 + k < n) ? x[k] : 0;
 }
 __device__ __forceinline__ void scan_store(const int (&v)[4], int n, int32_t *out,
                                            int32_t *wave_tot) {
@@ -117,14 +127,18 @@ __device__ void block_counts(const int32_t *__restrict__ packed, int K, int e_ou
   __syncthreads();  // every wave done (lds_mask may share LDS with routing scratch)
   for (int e = tid; e < e_out; e += THREADS) lds_mask[e] = 0u;
   __syncthreads();  // also orders this block's output stores before the reads below
-  const int n = ntok * K;
+  const int n = ntok * K;  // >= 1
   const int32_t *pk = packed + t_begin * K;
   int ev[PER], tv[PER];
+#pragma unroll
+  for (int h = 0; h < PER; ++h) {  // clamped, unconditional loads: one round trip
+    const int i = tid + h * THREADS;
+    ev[h] = pk[i < n ? i : n - 1] >> 16;
+  }
 #pragma unroll
   for (int h = 0; h < PER; ++h) {
     const int i = tid + h * THREADS;
     if (i < n) {
-      ev[h] = pk[i] >> 16;
       tv[h] = i / K;
       atomicOr(&lds_mask[ev[h]], 1u << tv[h]);
     }
@@ -347,8 +361,8 @@ __global__ __launch_bounds__(ROWS_BLOCK, 8) void route_rows_kernel(
     } wave[ROWS_WAVES];
     uint32_t mask[MOE_ROUTE_MAX_EXPERTS];
   } lds;
-  __shared__ int bad_bias;
-  const bool ok = rows::stage_bias<ROWS_BLOCK>(bias, bias_lds, &bad_bias);  // all threads
+  __shared__ int bad_bias[ROWS_WAVES];
+  const bool ok = rows::stage_bias<ROWS_BLOCK>(bias, bias_lds, bad_bias);  // all threads
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int64_t tb = (int64_t)blockIdx.x * ROWS_TOKENS_PER_BLOCK;

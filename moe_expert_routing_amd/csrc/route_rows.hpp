@@ -157,24 +157,34 @@ __device__ __forceinline__ void group_ranks(KT a, KT b, int &ra, int &rb) {
 
 // Stages fl32(b + 3) (in expert order) for a block of THREADS threads;
 // returns false (block-uniform) when some bias lies outside [-1, 500),
-// where the key encoding does not hold. `bad` is an LDS word.
+// where the key encoding does not hold. `bad` holds one LDS word per wave.
+// Every load is issued before the first is used (clamped indices, no
+// branches), so the staging costs one memory round trip.
 template <int THREADS>
 __device__ __forceinline__ bool stage_bias(const float *__restrict__ bias, float *lds, int *bad) {
-  if (threadIdx.x == 0) *bad = 0;
-  __syncthreads();
+  constexpr int N = (E + THREADS - 1) / THREADS;
+  float bb[N];
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    const int e = (int)threadIdx.x + k * THREADS;
+    bb[k] = bias[e < E ? e : E - 1] + BIAS_SHIFT;
+  }
   bool ok = true;
 #pragma unroll
-  for (int k = 0; k < (E + THREADS - 1) / THREADS; ++k) {
-    const int e = threadIdx.x + k * THREADS;
+  for (int k = 0; k < N; ++k) {
+    const int e = (int)threadIdx.x + k * THREADS;
     if (e < E) {
-      const float bb = bias[e] + BIAS_SHIFT;
-      ok = ok && (bb >= 2.0f) && (bb < 503.0f);
-      lds[e] = bb;
+      ok = ok && (bb[k] >= 2.0f) && (bb[k] < 503.0f);
+      lds[e] = bb[k];
     }
   }
-  if (!ok) *bad = 1;
+  const bool wave_bad = __ballot(!ok) != 0ull;
+  if ((threadIdx.x & 63) == 0) bad[threadIdx.x >> 6] = wave_bad ? 1 : 0;
   __syncthreads();
-  return *bad == 0;
+  int any = 0;
+#pragma unroll
+  for (int w = 0; w < THREADS / 64; ++w) any |= bad[w];
+  return any == 0;
 }
 
 // Streams the lane's 56 experts of the token at `row`: keys into the sorted
