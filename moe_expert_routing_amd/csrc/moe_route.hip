@@ -352,7 +352,7 @@ __global__ __launch_bounds__(ROWS_BLOCK, 8) void route_rows_kernel(
     const float *__restrict__ logits, const float *__restrict__ bias, int T, RouteParams p,
     int32_t *__restrict__ ids, float *__restrict__ wts, int32_t *__restrict__ packed,
     PrefillCounts pc) {
-  __shared__ float bias_lds[rows::E];
+  __shared__ float bias_lds[2][rows::E];  // fl32(b + B) of each key window
   // routing scratch, reused for the tile counts once every wave is done
   __shared__ union {
     union {
@@ -362,16 +362,19 @@ __global__ __launch_bounds__(ROWS_BLOCK, 8) void route_rows_kernel(
     uint32_t mask[MOE_ROUTE_MAX_EXPERTS];
   } lds;
   __shared__ int bad_bias[ROWS_WAVES];
-  const bool ok = rows::stage_bias<ROWS_BLOCK>(bias, bias_lds, bad_bias);  // all threads
+  const int window = rows::stage_bias<ROWS_BLOCK>(bias, bias_lds[0], bias_lds[1], bad_bias);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int64_t tb = (int64_t)blockIdx.x * ROWS_TOKENS_PER_BLOCK;
   const int64_t t0 = tb + 4 * wave;
   if (t0 < T) {
     uint32_t redo = 0xFu;
-    if (ok)
-      redo = rows::route_rows4(logits, bias, bias_lds, T, t0, p, lane, &lds.wave[wave].r, ids,
-                               wts, packed);
+    if (window == 0)
+      redo = rows::route_rows4<0>(logits, bias, bias_lds[0], T, t0, p, lane, &lds.wave[wave].r, ids,
+                                  wts, packed);
+    else if (window == 1)
+      redo = rows::route_rows4<1>(logits, bias, bias_lds[1], T, t0, p, lane, &lds.wave[wave].r, ids,
+                                  wts, packed);
     redo = (uint32_t)__builtin_amdgcn_readfirstlane((int)redo);
     while (redo) {
       const int r = __builtin_ctz(redo);

@@ -17,12 +17,17 @@
 // so the four lanes of a group read 64 contiguous bytes per load, and expert
 // ids increase with the slot.
 //
-// Keys. v = fl32(s~ + fl32(b + 3)) with s~ the hardware exp2/rcp sigmoid.
-// Whenever b >= -1, v lies in [2, 512), a range in which the top 6 bits of
-// the binary32 pattern are constant, so
+// Keys. v = fl32(s~ + fl32(b + B)) with s~ the hardware exp2/rcp sigmoid and a
+// constant shift B that puts v in a window of eight binades whose binary32
+// patterns share their top 6 bits (a window that starts at a multiple of
+// 2^26), so
 //   key = (bits(v) << 6) | (63 - q)
 // orders by v at full binary32 resolution, then by lower slot (lower id).
-// |v - (sp + 3)| <= row_err(v) (sp the exact biased score); see row_err.
+// Two windows (KeyWindow): B = 1/2, v in [2^-7, 2), for biases in
+// [-0.49, 0.49], which keeps the top scores (v in [1, 2)) at a resolution of
+// 2^-23; otherwise B = 3, v in [2, 512), for biases in [-1, 500). Each block
+// picks one from the biases it stages.
+// |v - (sp + B)| <= row_err(v, B) (sp the exact biased score).
 //
 // Selection.
 //  1. Each lane keeps its top-8 keys of each pass (v_max_u32 + seven
@@ -62,7 +67,19 @@ constexpr int PP = 8;       // keys kept per lane and pass
 constexpr int POOL = 10;    // merged keys of the kept groups per lane
 constexpr int MAX_K = 16;   // top_k handled by this path
 constexpr int MAX_CAND = 32;  // exact candidates per row in the refinement
-constexpr float BIAS_SHIFT = 3.0f;
+// Key windows: the shift B, the first bit pattern of the window and the range
+// that fl32(b + B) must stay in (so that v = s~ + fl32(b + B) stays inside).
+template <int W> struct KeyWindow;
+template <> struct KeyWindow<0> {  // v in [2^-7, 2)
+  static constexpr float shift = 0.5f;
+  static constexpr uint32_t base = 0x3C000000u;  // bits(2^-7) = 15 * 2^26
+  static constexpr float lo = 0x1p-7f, hi = 0.99f;
+};
+template <> struct KeyWindow<1> {  // v in [2, 512)
+  static constexpr float shift = 3.0f;
+  static constexpr uint32_t base = 0x40000000u;  // bits(2) = 16 * 2^26
+  static constexpr float lo = 2.0f, hi = 503.0f;
+};
 constexpr int PREFETCH = 3;   // float4 loads in flight per lane
 
 constexpr int DPP_ROR4 = 0x124, DPP_ROR8 = 0x128, DPP_ROR12 = 0x12C;
@@ -78,17 +95,24 @@ struct RowScratch {
   float kth[4];
 };
 
-// |v - (sp + 3)| for a key value v, sp = RN32(RN32(sigma(x)) + b): the fast
-// sigmoid error (<= FAST_SIG_ERR) and three binary32 roundings (of b + 3,
-// of s~ + (b + 3), of the exact s + b), each at most 2^-24 v, with margin.
-__device__ __forceinline__ float row_err(float v) { return 1.01f * FAST_SIG_ERR + 0x1p-22f * v; }
-// Same for a group score of up to two key values plus its own rounding and
-// the rounding of the exact group score.
-__device__ __forceinline__ float row_group_err(float v) {
-  return 2.02f * FAST_SIG_ERR + 0x1p-21f * v;
+// |v - (sp + B)| for a key value v, sp = RN32(RN32(sigma(x)) + b), sh = B > 0:
+// the fast sigmoid error (<= FAST_SIG_ERR) and three binary32 roundings, of
+// b + B and of s~ + (b + B) (each at most 2^-24 v) and of the exact s + b
+// (at most 2^-24 |sp| <= 2^-24 (v + sh)), with margin.
+__device__ __forceinline__ float row_err(float v, float sh) {
+  return 1.01f * FAST_SIG_ERR + 0x1p-24f * (3.03f * v + 1.01f * sh);
+}
+// Same for a group score g = fl32(v1 + v2) of up to two key values: both key
+// errors, the rounding of g (2^-24 g) and that of the exact group score
+// (2^-24 |gs| <= 2^-24 (g + 2 sh)), with margin.
+__device__ __forceinline__ float row_group_err(float g, float sh) {
+  return 2.02f * FAST_SIG_ERR + 0x1p-24f * (5.1f * g + 4.1f * sh);
 }
 
-__device__ __forceinline__ float key_v(uint32_t k) { return __uint_as_float((k >> 6) | 0x40000000u); }
+template <int W>
+__device__ __forceinline__ float key_v(uint32_t k) {
+  return __uint_as_float((k >> 6) | KeyWindow<W>::base);
+}
 
 // Expert id of a key held by the lane (quad c, sub).
 __device__ __forceinline__ int key_expert(uint32_t k, int c, int sub) {
@@ -155,36 +179,41 @@ __device__ __forceinline__ void group_ranks(KT a, KT b, int &ra, int &rb) {
   }
 }
 
-// Stages fl32(b + 3) (in expert order) for a block of THREADS threads;
-// returns false (block-uniform) when some bias lies outside [-1, 500),
-// where the key encoding does not hold. `bad` holds one LDS word per wave.
-// Every load is issued before the first is used (clamped indices, no
-// branches), so the staging costs one memory round trip.
+// Stages fl32(b + B) (in expert order) for a block of THREADS threads, for
+// both key windows (lds0: B = 1/2, lds1: B = 3). Returns the window every
+// bias fits (0 preferred), or -1 (block-uniform) when some bias fits neither
+// (or is not finite). `bad` holds one LDS word per wave. Every load is issued
+// before the first is used (clamped indices, no branches), so the staging
+// costs one memory round trip.
 template <int THREADS>
-__device__ __forceinline__ bool stage_bias(const float *__restrict__ bias, float *lds, int *bad) {
+__device__ __forceinline__ int stage_bias(const float *__restrict__ bias, float *lds0, float *lds1,
+                                          int *bad) {
   constexpr int N = (E + THREADS - 1) / THREADS;
   float bb[N];
 #pragma unroll
   for (int k = 0; k < N; ++k) {
     const int e = (int)threadIdx.x + k * THREADS;
-    bb[k] = bias[e < E ? e : E - 1] + BIAS_SHIFT;
+    bb[k] = bias[e < E ? e : E - 1];
   }
-  bool ok = true;
+  bool ok0 = true, ok1 = true;
 #pragma unroll
   for (int k = 0; k < N; ++k) {
     const int e = (int)threadIdx.x + k * THREADS;
     if (e < E) {
-      ok = ok && (bb[k] >= 2.0f) && (bb[k] < 503.0f);
-      lds[e] = bb[k];
+      const float v0 = bb[k] + KeyWindow<0>::shift, v1 = bb[k] + KeyWindow<1>::shift;
+      ok0 = ok0 && (v0 >= KeyWindow<0>::lo) && (v0 <= KeyWindow<0>::hi);
+      ok1 = ok1 && (v1 >= KeyWindow<1>::lo) && (v1 < KeyWindow<1>::hi);
+      lds0[e] = v0;
+      lds1[e] = v1;
     }
   }
-  const bool wave_bad = __ballot(!ok) != 0ull;
-  if ((threadIdx.x & 63) == 0) bad[threadIdx.x >> 6] = wave_bad ? 1 : 0;
+  const bool bad0 = __ballot(!ok0) != 0ull, bad1 = __ballot(!ok1) != 0ull;
+  if ((threadIdx.x & 63) == 0) bad[threadIdx.x >> 6] = (bad0 ? 1 : 0) | (bad1 ? 2 : 0);
   __syncthreads();
   int any = 0;
 #pragma unroll
   for (int w = 0; w < THREADS / 64; ++w) any |= bad[w];
-  return any == 0;
+  return (any & 1) == 0 ? 0 : ((any & 2) == 0 ? 1 : -1);
 }
 
 // Streams the lane's 56 experts of the token at `row`: keys into the sorted
@@ -226,19 +255,22 @@ __device__ __forceinline__ void stream_pools(const float *__restrict__ row,
 
 // Approximate group stage: the quad's top-2 of each pass, group scores,
 // kept flags, and whether the choice is certified.
+template <int W>
 __device__ __forceinline__ bool approx_groups(const uint32_t (&a)[PP], const uint32_t (&b)[PP],
                                               const RouteParams &p, int c, bool &kept_a,
                                               bool &kept_b) {
+  constexpr float sh = KeyWindow<W>::shift;
   uint32_t a1 = a[0], a2 = a[1], b1 = b[0], b2 = b[1];
   top2_merge(a1, a2, dpp<DPP_XOR1>(a1), dpp<DPP_XOR1>(a2));
   top2_merge(a1, a2, dpp<DPP_XOR2>(a1), dpp<DPP_XOR2>(a2));
   top2_merge(b1, b2, dpp<DPP_XOR1>(b1), dpp<DPP_XOR1>(b2));
   top2_merge(b1, b2, dpp<DPP_XOR2>(b1), dpp<DPP_XOR2>(b2));
-  const float ga = (p.topn == 2) ? key_v(a1) + key_v(a2) : key_v(a1);  // in [2, 1030)
-  const float gb = (p.topn == 2) ? key_v(b1) + key_v(b2) : key_v(b1);
-  // unique group keys: score bits (the top 3 bits are constant), then lower group
-  const uint32_t ka = (__float_as_uint(ga) << 3) | (uint32_t)(7 - c);
-  const uint32_t kb = (__float_as_uint(gb) << 3) | (uint32_t)(3 - c);
+  const float ga = (p.topn == 2) ? key_v<W>(a1) + key_v<W>(a2) : key_v<W>(a1);
+  const float gb = (p.topn == 2) ? key_v<W>(b1) + key_v<W>(b2) : key_v<W>(b1);
+  // unique group keys: score bits above the window start (below 9 * 2^23, a
+  // window and one binade more, so three bits to spare), then lower group
+  const uint32_t ka = ((__float_as_uint(ga) - KeyWindow<W>::base) << 3) | (uint32_t)(7 - c);
+  const uint32_t kb = ((__float_as_uint(gb) - KeyWindow<W>::base) << 3) | (uint32_t)(3 - c);
   int ra, rb;
   group_ranks(ka, kb, ra, rb);
   kept_a = ra < p.TG;
@@ -249,7 +281,7 @@ __device__ __forceinline__ bool approx_groups(const uint32_t (&a)[PP], const uin
   const float kmin = __uint_as_float(
       row_min(umin(kept_a ? ba : 0x7F7FFFFFu, kept_b ? bb : 0x7F7FFFFFu)));
   const float dmax = __uint_as_float(row_max(umax(kept_a ? 0u : ba, kept_b ? 0u : bb)));
-  return kmin - row_group_err(kmin) > dmax + row_group_err(dmax);
+  return kmin - row_group_err(kmin, sh) > dmax + row_group_err(dmax, sh);
 }
 
 // Descending compare-exchange.
@@ -323,32 +355,75 @@ __device__ __forceinline__ void row_outputs(bool out, uint2 sl, const RouteParam
 }
 
 // Number of pool entries (sorted by key) whose value is >= thr.
+template <int W>
 __device__ __forceinline__ int pool_count_ge(const uint32_t (&pl)[PP], double thr) {
   int n = 0;
 #pragma unroll
-  for (int i = 0; i < PP; ++i) n += ((double)key_v(pl[i]) >= thr) ? 1 : 0;
+  for (int i = 0; i < PP; ++i) n += ((double)key_v<W>(pl[i]) >= thr) ? 1 : 0;
   return n;
 }
 
-// Exact top-2 (ord keys, with multiplicity) of the first n entries of pl,
-// merged over the quad (the group's four lanes).
-__device__ __forceinline__ void exact_top2(const float *__restrict__ row,
-                                           const float *__restrict__ bias_g,
-                                           const uint32_t (&pl)[PP], int n, int c, int sub,
-                                           uint32_t &t1, uint32_t &t2) {
-  t1 = t2 = 0u;
+// Exact score (ord key) of expert e.
+__device__ __forceinline__ uint32_t exact_key(float x, float b) {
+  return ord_f32(sigmoid_rn32(x) + b);
+}
+
+// Exact top-2 (ord keys, with multiplicity) of the first na entries of pool
+// a and the first nb of pool b, each merged over the quad (the group's four
+// lanes). The logits and biases of the first EXACT_PRELOAD entries of both
+// pools are loaded together, before any is used, so the usual case costs one
+// memory round trip; entries beyond them (rare) follow one by one.
+constexpr int EXACT_PRELOAD = 2;
+__device__ __forceinline__ void exact_top2_pair(const float *__restrict__ row,
+                                                const float *__restrict__ bias_g,
+                                                const uint32_t (&a)[PP], int na,
+                                                const uint32_t (&b)[PP], int nb, int c, int sub,
+                                                uint32_t &ta1, uint32_t &ta2, uint32_t &tb1,
+                                                uint32_t &tb2) {
+  ta1 = ta2 = tb1 = tb2 = 0u;
+  float xa[EXACT_PRELOAD], ya[EXACT_PRELOAD], xb[EXACT_PRELOAD], yb[EXACT_PRELOAD];
 #pragma unroll
-  for (int i = 0; i < PP; ++i) {
-    if (!__ballot(i < n)) break;
-    if (i < n) {
-      const int e = key_expert(pl[i], c, sub);
-      const uint32_t o = ord_f32(sigmoid_rn32(row[e]) + bias_g[e]);
-      t2 = umax(t2, umin(t1, o));
-      t1 = umax(t1, o);
+  for (int i = 0; i < EXACT_PRELOAD; ++i) {  // in-range ids only: expert 0 past n
+    const int ea = i < na ? key_expert(a[i], c, sub) : 0;
+    const int eb = i < nb ? key_expert(b[i], c, sub) : 0;
+    xa[i] = row[ea];
+    ya[i] = bias_g[ea];
+    xb[i] = row[eb];
+    yb[i] = bias_g[eb];
+  }
+#pragma unroll
+  for (int i = 0; i < EXACT_PRELOAD; ++i) {
+    if (i < na) {
+      const uint32_t o = exact_key(xa[i], ya[i]);
+      ta2 = umax(ta2, umin(ta1, o));
+      ta1 = umax(ta1, o);
+    }
+    if (i < nb) {
+      const uint32_t o = exact_key(xb[i], yb[i]);
+      tb2 = umax(tb2, umin(tb1, o));
+      tb1 = umax(tb1, o);
     }
   }
-  top2_merge(t1, t2, dpp<DPP_XOR1>(t1), dpp<DPP_XOR1>(t2));
-  top2_merge(t1, t2, dpp<DPP_XOR2>(t1), dpp<DPP_XOR2>(t2));
+#pragma unroll
+  for (int i = EXACT_PRELOAD; i < PP; ++i) {
+    if (!__ballot(i < na || i < nb)) break;
+    if (i < na) {
+      const int e = key_expert(a[i], c, sub);
+      const uint32_t o = exact_key(row[e], bias_g[e]);
+      ta2 = umax(ta2, umin(ta1, o));
+      ta1 = umax(ta1, o);
+    }
+    if (i < nb) {
+      const int e = key_expert(b[i], c, sub);
+      const uint32_t o = exact_key(row[e], bias_g[e]);
+      tb2 = umax(tb2, umin(tb1, o));
+      tb1 = umax(tb1, o);
+    }
+  }
+  top2_merge(ta1, ta2, dpp<DPP_XOR1>(ta1), dpp<DPP_XOR1>(ta2));
+  top2_merge(ta1, ta2, dpp<DPP_XOR2>(ta1), dpp<DPP_XOR2>(ta2));
+  top2_merge(tb1, tb2, dpp<DPP_XOR1>(tb1), dpp<DPP_XOR1>(tb2));
+  top2_merge(tb1, tb2, dpp<DPP_XOR2>(tb1), dpp<DPP_XOR2>(tb2));
 }
 
 // Exact refinement of the rows with `need` set (call with the whole wave).
@@ -360,6 +435,7 @@ __device__ __forceinline__ void exact_top2(const float *__restrict__ row,
 // decide on exact scores, so they only fail when a pool is too short or the
 // candidates exceed MAX_CAND. Returns true (row-uniform) when the row has
 // been written.
+template <int W>
 __device__ __forceinline__ bool refine_rows(const float *__restrict__ row,
                                             const float *__restrict__ bias_g,
                                             const uint32_t (&a)[PP], const uint32_t (&b)[PP],
@@ -370,6 +446,7 @@ __device__ __forceinline__ bool refine_rows(const float *__restrict__ row,
                                             int32_t *__restrict__ packed) {
   const int K = p.K;
   const int c = u >> 2, sub = u & 3;
+  constexpr float sh = KeyWindow<W>::shift;
   if (need && u == 0) atomicAdd(&g_refined_tokens, 1ull);
   bool fail = false;
   bool kept_a = kept_a_in, kept_b = kept_b_in;
@@ -384,14 +461,15 @@ __device__ __forceinline__ bool refine_rows(const float *__restrict__ row,
     top2_merge(a1, a2, dpp<DPP_XOR2>(a1), dpp<DPP_XOR2>(a2));
     top2_merge(b1, b2, dpp<DPP_XOR1>(b1), dpp<DPP_XOR1>(b2));
     top2_merge(b1, b2, dpp<DPP_XOR2>(b1), dpp<DPP_XOR2>(b2));
-    const double thra = (double)key_v(p.topn == 2 ? a2 : a1) - 2.0 * (double)row_err(key_v(a1));
-    const double thrb = (double)key_v(p.topn == 2 ? b2 : b1) - 2.0 * (double)row_err(key_v(b1));
-    const int na = regroup ? pool_count_ge(a, thra) : 0;
-    const int nb = regroup ? pool_count_ge(b, thrb) : 0;
+    const double thra =
+        (double)key_v<W>(p.topn == 2 ? a2 : a1) - 2.0 * (double)row_err(key_v<W>(a1), sh);
+    const double thrb =
+        (double)key_v<W>(p.topn == 2 ? b2 : b1) - 2.0 * (double)row_err(key_v<W>(b1), sh);
+    const int na = regroup ? pool_count_ge<W>(a, thra) : 0;
+    const int nb = regroup ? pool_count_ge<W>(b, thrb) : 0;
     fail = row_max((na >= PP || nb >= PP) ? 1u : 0u) != 0u;
     uint32_t ta1, ta2, tb1, tb2;
-    exact_top2(row, bias_g, a, na, c, sub, ta1, ta2);
-    exact_top2(row, bias_g, b, nb, c, sub, tb1, tb2);
+    exact_top2_pair(row, bias_g, a, na, b, nb, c, sub, ta1, ta2, tb1, tb2);
     const float gxa = (p.topn == 2) ? ord_inv(ta1) + ord_inv(ta2) : ord_inv(ta1);
     const float gxb = (p.topn == 2) ? ord_inv(tb1) + ord_inv(tb2) : ord_inv(tb1);
     int ra, rb;
@@ -410,10 +488,10 @@ __device__ __forceinline__ bool refine_rows(const float *__restrict__ row,
   }
 
   // ---- exact top_k from the candidates within the error band ----------------------
-  const float vm = key_v(M);
-  const double thb = (double)vm - 2.0 * (double)row_err(vm);
-  const int ca = (need && kept_a) ? pool_count_ge(a, thb) : 0;
-  const int cb = (need && kept_b) ? pool_count_ge(b, thb) : 0;
+  const float vm = key_v<W>(M);
+  const double thb = (double)vm - 2.0 * (double)row_err(vm, sh);
+  const int ca = (need && kept_a) ? pool_count_ge<W>(a, thb) : 0;
+  const int cb = (need && kept_b) ? pool_count_ge<W>(b, thb) : 0;
   fail = fail || row_max((ca >= PP || cb >= PP) ? 1u : 0u) != 0u;
   const int c2 = ca + cb;
   const int mc = (int)row_sum((uint32_t)c2);
@@ -467,9 +545,9 @@ __device__ __forceinline__ bool refine_rows(const float *__restrict__ row,
   }
   wave_lds_sync();
   // every expert outside the candidates has key value < thb, so an exact
-  // score below thb - 3 + row_err(thb); the K-th winner must beat it (it
+  // score below thb - B + row_err(thb); the K-th winner must beat it (it
   // does whenever the arithmetic above is right; kept as a guard)
-  const double bound = thb - 3.0 + (1.01 * (double)FAST_SIG_ERR + 0x1p-22 * thb);
+  const double bound = thb - (double)sh + (double)row_err((float)thb, sh) * 1.01;
   const bool ok = ok_m && (double)L->kth[r] > bound;
   uint2 sl = make_uint2(0u, 0u);
   if (ok && u < K) sl = L->slot[r][u];
@@ -478,8 +556,10 @@ __device__ __forceinline__ bool refine_rows(const float *__restrict__ row,
 }
 
 // Routes tokens t0 .. t0+3 (rows beyond T are computed on token T-1 and
-// discarded). Returns a 4-bit mask of the rows that must be routed again by
-// the one-token-per-wave path; every other valid row has been written.
+// discarded); bias_lds holds fl32(b + B) of key window W from stage_bias.
+// Returns a 4-bit mask of the rows that must be routed again by the
+// one-token-per-wave path; every other valid row has been written.
+template <int W>
 __device__ __forceinline__ uint32_t route_rows4(const float *__restrict__ logits,
                                                 const float *__restrict__ bias_g,
                                                 const float *__restrict__ bias_lds, int T,
@@ -506,7 +586,7 @@ __device__ __forceinline__ uint32_t route_rows4(const float *__restrict__ logits
   stream_pools(row, bias_lds, c, sub, a, b);
   __builtin_amdgcn_s_setprio(1);
   bool kept_a, kept_b;
-  const bool groups_ok = approx_groups(a, b, p, c, kept_a, kept_b);  // row-uniform
+  const bool groups_ok = approx_groups<W>(a, b, p, c, kept_a, kept_b);  // row-uniform
   bool fail = !groups_ok;
   uint32_t m[POOL];
   merge_kept(a, b, kept_a, kept_b, m);
@@ -549,9 +629,9 @@ __device__ __forceinline__ uint32_t route_rows4(const float *__restrict__ logits
     L->ekey[r][u] = ((uint64_t)ord_f32(my_sp) << 32) | (uint64_t)(~(uint32_t)my_id);
   }
   // every expert outside the winners has a key below M: its exact score is at
-  // most key_v(M) - 3 + row_err(key_v(M)); the weakest winner must beat that
-  const float vm = key_v(M);
-  const double bound = (double)vm - 3.0 + (double)row_err(vm);
+  // most key_v(M) - B + row_err(key_v(M)); the weakest winner must beat that
+  const float vm = key_v<W>(M);
+  const double bound = (double)vm - (double)KeyWindow<W>::shift + (double)row_err(vm, KeyWindow<W>::shift);
   const uint32_t weakest = row_min(act ? ord_f32(my_sp) : 0xFFFFFFFFu);
   const bool boundary_ok = (double)ord_inv(weakest) > bound;
   wave_lds_sync();
@@ -577,7 +657,7 @@ __device__ __forceinline__ uint32_t route_rows4(const float *__restrict__ logits
   if (__ballot(need)) {
     __builtin_amdgcn_s_setprio(3);
     wave_lds_sync();
-    done = refine_rows(row, bias_g, a, b, need, groups_ok, kept_a, kept_b, M, p, r, u, t, L, ids,
+    done = refine_rows<W>(row, bias_g, a, b, need, groups_ok, kept_a, kept_b, M, p, r, u, t, L, ids,
                        wts, packed) ||
            done;
   }

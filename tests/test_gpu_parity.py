@@ -352,3 +352,19 @@ def test_prefill_rows_all_tied_reroute():
     say("case all tied T=100")
     assert_parity(run_case(c), oracle_case(c), c.name)
     assert M.path_tokens(M.PATH_REROUTED, reset=True) == 100
+
+
+@pytest.mark.parametrize("offset,all_rerouted", [
+    (0.45, False), (-0.45, False), (1.5, False), (-0.9, False), (600.0, True)])
+def test_prefill_rows_key_windows(offset, all_rerouted):
+    """Biases near both edges of the narrow key window (b + 1/2), inside the
+    wide one (b + 3), and outside both, where every row goes through the exact
+    per-token pipeline; the result is the oracle's in every case."""
+    c = W.random_case(200, seed=31)
+    bias = (c.bias + np.float32(offset)).astype(np.float32)
+    case = W.RouteCase(f"bias_offset_{offset}", c.logits, bias)
+    M.path_tokens(M.PATH_REROUTED, reset=True)
+    say(f"case bias offset {offset} T=200")
+    assert_parity(run_case(case), oracle_case(case), case.name)
+    rerouted = M.path_tokens(M.PATH_REROUTED, reset=True)
+    assert (rerouted == 200) if all_rerouted else (rerouted < 200), rerouted
