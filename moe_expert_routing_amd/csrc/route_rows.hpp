@@ -87,7 +87,7 @@ constexpr int DPP_ROR4 = 0x124, DPP_ROR8 = 0x128, DPP_ROR12 = 0x12C;
 // Per-wave LDS of the row path, by row: winner / candidate ids, exact keys
 // and scores, the final (id, s) by slot.
 struct RowScratch {
-  int32_t id[4][MAX_K];
+  uint2 win[4][MAX_K];  // winner of extraction round k: (key, lane in the row)
   int32_t cnt[4][LANES];
   int32_t cand[4][MAX_CAND];
   unsigned long long ekey[4][MAX_CAND];
@@ -316,8 +316,10 @@ __device__ __forceinline__ void merge_kept(const uint32_t (&a)[PP], const uint32
 
 // top_k + 1 rounds of row maximum over the heads of m (sorted, descending).
 // rounds: bit (K - round) set when this lane won that round; returns the
-// last maximum (the (top_k+1)-th key).
-__device__ __forceinline__ uint32_t extract(const uint32_t (&m)[POOL], int K, uint32_t &rounds) {
+// last maximum (the (top_k+1)-th key). With win, the lane that wins round
+// rd < K writes (its key, u = its lane in the row) to win[rd].
+__device__ __forceinline__ uint32_t extract(const uint32_t (&m)[POOL], int K, uint32_t &rounds,
+                                            uint2 *win = nullptr, int u = 0) {
   uint32_t q[POOL];
 #pragma unroll
   for (int i = 0; i < POOL; ++i) q[i] = m[i];
@@ -325,10 +327,11 @@ __device__ __forceinline__ uint32_t extract(const uint32_t (&m)[POOL], int K, ui
   rounds = 0u;
   for (int rd = 0; rd <= K; ++rd) {
     M = row_max(q[0]);
-    const bool win = q[0] == M;
-    rounds = rounds + rounds + (win ? 1u : 0u);
+    const bool won = q[0] == M;
+    if (win && won && rd < K) win[rd] = make_uint2(M, (uint32_t)u);
+    rounds = rounds + rounds + (won ? 1u : 0u);
 #pragma unroll
-    for (int i = 0; i < POOL - 1; ++i) q[i] = win ? q[i + 1] : q[i];
+    for (int i = 0; i < POOL - 1; ++i) q[i] = won ? q[i + 1] : q[i];
   }
   return M;
 }
@@ -591,30 +594,14 @@ __device__ __forceinline__ uint32_t route_rows4(const float *__restrict__ logits
   uint32_t m[POOL];
   merge_kept(a, b, kept_a, kept_b, m);
   uint32_t rounds;
-  const uint32_t M = extract(m, K, rounds);
+  const uint32_t M = extract(m, K, rounds, L->win[r], u);
   const int pops = __popc(rounds);
   const uint32_t total = row_sum((uint32_t)pops);
   // exactly K+1 entries taken (no equal keys) and the merged pool not used up
   fail = fail || total != (uint32_t)(K + 1) || pops >= POOL;
-
-  // ---- winners (the first K extracted) to LDS: expert ids ----------------------
-  uint32_t rem = rounds >> 1;  // drop round K (the best non-winner)
-  int pa = 0, pb = 0;          // popped entries of each pass (round K included)
-#pragma unroll
-  for (int i = 0; i < POOL - 1; ++i) {
-    if (!__ballot(i < pops)) break;
-    if (i < pops) {
-      const uint32_t key = m[i];
-      if (key_pass1(key)) ++pb; else ++pa;
-      if (rem != 0u) {
-        const int hb = 31 - __clz(rem);  // earliest remaining round
-        rem ^= 1u << hb;
-        L->id[r][K - 1 - hb] = key_expert(key, c, sub);
-      }
-    }
-  }
-  // a pass pool used up may hide further keys of that group
-  fail = fail || pa >= PP || pb >= PP;
+  // a pass pool whose last key was taken (every key >= M was taken) may hide
+  // further keys of that group
+  fail = fail || (kept_a && a[PP - 1] >= M) || (kept_b && b[PP - 1] >= M);
   wave_lds_sync();
 
   // ---- exact scores of the winners; exact order by (sp desc, id asc) ---------------
@@ -623,7 +610,8 @@ __device__ __forceinline__ uint32_t route_rows4(const float *__restrict__ logits
   int my_id = 0;
   float my_s = 0.0f, my_sp = 0.0f;
   if (act) {
-    my_id = L->id[r][u];
+    const uint2 w = L->win[r][u];  // winner of round u: key and the lane holding it
+    my_id = key_expert(w.x, (int)(w.y >> 2), (int)(w.y & 3));
     my_s = sigmoid_rn32(row[my_id]);
     my_sp = my_s + bias_g[my_id];
     L->ekey[r][u] = ((uint64_t)ord_f32(my_sp) << 32) | (uint64_t)(~(uint32_t)my_id);

@@ -368,3 +368,32 @@ def test_prefill_rows_key_windows(offset, all_rerouted):
     assert_parity(run_case(case), oracle_case(case), case.name)
     rerouted = M.path_tokens(M.PATH_REROUTED, reset=True)
     assert (rerouted == 200) if all_rerouted else (rerouted < 200), rerouted
+
+
+@pytest.mark.parametrize("kind", ["reroute", "refine"])
+def test_prefill_many_blocks_with_slow_rows(kind):
+    """More route blocks (3075 of 16 tokens) than the GPU holds at once, a
+    ragged last block, and rows that leave the fast path scattered over all
+    of them: fully tied rows (routed again one token per wave) or rows with
+    exact twins near the 16th place (refined). Everything matches the
+    oracle."""
+    T = 16 * 3074 + 5
+    rng = np.random.default_rng(20261207)
+    logits = rng.standard_normal((T, 896), dtype=np.float32)
+    if kind == "reroute":
+        bias = np.zeros(896, np.float32)
+        logits[::409] = np.float32(0.5)
+        path = M.PATH_REROUTED
+    else:
+        src = W.decode_sweep(256, 0)
+        bias = src.bias
+        rows = np.arange(1, T, 97)
+        logits[rows] = src.logits[rows % 256]
+        path = M.PATH_REFINED
+    c = W.RouteCase(f"many_tiles_{kind}", logits, bias, off=0, cnt=112)
+    M.path_tokens(path, reset=True)
+    say(f"case many tiles per block T={T} kind={kind}")
+    assert_parity(run_case(c), oracle_case(c), c.name)
+    n = M.path_tokens(path, reset=True)
+    say(f"{kind}: {n} tokens off the fast path")
+    assert n > 0
