@@ -61,31 +61,38 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Exclusive scan of in[0..n) (n <= 1024) into out[0..n] in LDS, out[n] =
-// total, in two steps so that a caller can issue other loads between them:
-// scan_load reads this thread's 4 inputs; scan_store scans and writes.
-// All BLOCK threads must call both.
-// The loads take clamped indices and are unconditional, so all four are in
-// flight together (a guarded load becomes a branch that waits on its own).
-__device__ __forceinline__ void scan_load(const int32_t *in, int n, int (&v)[4]) {
+// total, by a block of THREADS threads (each takes 1024 / THREADS inputs), in
+// two steps so that a caller can issue other loads between them: scan_load
+// reads this thread's inputs; scan_store scans and writes. All THREADS
+// threads must call both; wave_tot holds THREADS / 64 words.
+// The loads take clamped indices and are unconditional, so all of them are
+// in flight together (a guarded load becomes a branch that waits on its own).
+template <int THREADS = BLOCK>
+__device__ __forceinline__ void scan_load(const int32_t *in, int n, int (&v)[1024 / THREADS]) {
+  constexpr int PER = 1024 / THREADS;
   if (n <= 0) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) v[k] = 0;
+    for (int k = 0; k < PER; ++k) v[k] = 0;
     return;
   }
-  int x[4];
+  int x[PER];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int idx = threadIdx.x * 4 + k;
+  for (int k = 0; k < PER; ++k) {
+    const int idx = threadIdx.x * PER + k;
     x[k] = in[idx < n ? idx : n - 1];
   }
 #pragma unroll
-  for (int k = 0; k < 4; ++k) v[k] = ((int)threadIdx.x * 4 + k < n) ? x[k] : 0;
+  for (int k = 0; k < PER; ++k) v[k] = ((int)threadIdx.x * PER + k < n) ? x[k] : 0;
 }
-__device__ __forceinline__ void scan_store(const int (&v)[4], int n, int32_t *out,
+template <int THREADS = BLOCK>
+__device__ __forceinline__ void scan_store(const int (&v)[1024 / THREADS], int n, int32_t *out,
                                            int32_t *wave_tot) {
+  constexpr int PER = 1024 / THREADS;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
-  const int s = v[0] + v[1] + v[2] + v[3];
+  int s = 0;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) s += v[k];
   const int incl = wave_inclusive_scan(s);
   if (lane == 63) wave_tot[wv] = incl;
   lds_barrier();
@@ -93,21 +100,22 @@ __device__ __forceinline__ void scan_store(const int (&v)[4], int n, int32_t *ou
   for (int w = 0; w < wv; ++w) wave_off += wave_tot[w];
   int run = wave_off + incl - s;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int idx = tid * 4 + k;
+  for (int k = 0; k < PER; ++k) {
+    const int idx = tid * PER + k;
     if (idx < n) out[idx] = run;
     run += v[k];
   }
-  if (tid == BLOCK - 1) out[n] = wave_off + incl;
+  if (tid == THREADS - 1) out[n] = wave_off + incl;
   lds_barrier();
 }
 
 // The same in one call (in may be LDS or global memory; in place allowed:
 // every read precedes every write).
+template <int THREADS = BLOCK>
 __device__ void block_exclusive_scan(const int32_t *in, int n, int32_t *out, int32_t *wave_tot) {
-  int v[4];
-  scan_load(in, n, v);
-  scan_store(v, n, out, wave_tot);
+  int v[1024 / THREADS];
+  scan_load<THREADS>(in, n, v);
+  scan_store<THREADS>(v, n, out, wave_tot);
 }
 
 // ---------------------------------------------------------------------------
@@ -219,28 +227,34 @@ __global__ __launch_bounds__(BLOCK) void mx_quant_kernel(QuantArgs qa) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode path: one launch for T <= 64.
+// Decode path: one launch for T <= 64, NW waves (one token each) per block.
+// With one routing block (T <= NW) the block builds the permutation right
+// after its own barrier; with several, every block publishes its outputs,
+// fences and takes a ticket, and the last one builds it. Blocks past the
+// routing blocks quantise the activations.
 // ---------------------------------------------------------------------------
-template <int NP, int LPG>
-__global__ __launch_bounds__(BLOCK) void route_decode_kernel(
+constexpr int DECODE_ONE_BLOCK_WAVES = 8;  // T <= 8: one routing block
+
+template <int NP, int LPG, int NW>
+__global__ __launch_bounds__(64 * NW) void route_decode_kernel(
     const float *__restrict__ logits, const float *__restrict__ bias, int T, RouteParams p,
     int32_t *__restrict__ ids, float *__restrict__ wts, int32_t *__restrict__ packed,
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
     int32_t *__restrict__ inv, uint32_t *__restrict__ ticket, QuantArgs qa) {
-  // blocks past the routing blocks quantise the activations (no ticket)
-  const int nroute = T > 0 ? (T + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK : 1;
+  constexpr int THREADS = 64 * NW;
+  const int nroute = T > 0 ? (T + NW - 1) / NW : 1;
   if ((int)blockIdx.x >= nroute) {
-    mx_quant_chunk(qa, (int64_t)(blockIdx.x - nroute) * QUANT_CHUNKS_PER_BLOCK + threadIdx.x);
+    mx_quant_chunk(qa, (int64_t)(blockIdx.x - nroute) * THREADS + threadIdx.x);
     return;
   }
   __shared__ unsigned long long mask[MOE_ROUTE_MAX_EXPERTS];
   __shared__ int32_t offs[MOE_ROUTE_MAX_EXPERTS + 1];
-  __shared__ int32_t wave_tot[WAVES_PER_BLOCK];
-  __shared__ WaveScratch scratch[WAVES_PER_BLOCK];
+  __shared__ int32_t wave_tot[NW];
+  __shared__ WaveScratch scratch[NW];
   __shared__ int is_last;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  const int t = blockIdx.x * WAVES_PER_BLOCK + wave;
+  const int t = blockIdx.x * NW + wave;
   if (t < T) {
     const float *row = logits + (size_t)t * p.E;
     float b[2 * NP], x[2 * NP];
@@ -248,17 +262,21 @@ __global__ __launch_bounds__(BLOCK) void route_decode_kernel(
     load_lane_layout<NP, LPG>(bias, p, lane, b);
     route_token<NP, LPG>(row, x, b, bias, p, lane, t, &scratch[wave], ids, wts, packed);
   }
-  // Publish this block's outputs, then take a ticket.
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) is_last = (atomicAdd(ticket, 1u) == (uint32_t)nroute - 1u);
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
+  if (nroute > 1) {
+    // Publish this block's outputs, then take a ticket.
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) is_last = (atomicAdd(ticket, 1u) == (uint32_t)nroute - 1u);
+    __syncthreads();
+    if (!is_last) return;
+    __threadfence();
+  } else {
+    __syncthreads();  // the only routing block: its own outputs, nothing to wait for
+  }
 
   // Every entry's output id, read once: PER loads per thread issued back to
   // back (indices past the end read the last entry and are not used).
-  constexpr int PER = (MOE_ROUTE_MAX_FUSED_TOKENS * MOE_ROUTE_MAX_TOPK + BLOCK - 1) / BLOCK;
+  constexpr int PER = (MOE_ROUTE_MAX_FUSED_TOKENS * MOE_ROUTE_MAX_TOPK + THREADS - 1) / THREADS;
   static_assert(MOE_ROUTE_MAX_FUSED_TOKENS * MOE_ROUTE_MAX_TOPK <= 2048, "entry range");
   const int n = T * p.K;
   // token of entry f = f / K as a multiply-high (exact for f < 2048, K <= 32)
@@ -268,40 +286,40 @@ __global__ __launch_bounds__(BLOCK) void route_decode_kernel(
   for (int h = 0; h < PER; ++h) ev[h] = 0;
   if (n > 0) {
 #pragma unroll
-    for (int h = 0; h < PER; ++h) ev[h] = packed[min((int)threadIdx.x + h * BLOCK, n - 1)];
+    for (int h = 0; h < PER; ++h) ev[h] = packed[min((int)threadIdx.x + h * THREADS, n - 1)];
   }
-  for (int i = threadIdx.x; i < p.e_out; i += BLOCK) mask[i] = 0ull;
+  for (int i = threadIdx.x; i < p.e_out; i += THREADS) mask[i] = 0ull;
 #pragma unroll
   for (int h = 0; h < PER; ++h) {
-    const int f = min((int)threadIdx.x + h * BLOCK, max(n - 1, 0));
+    const int f = min((int)threadIdx.x + h * THREADS, max(n - 1, 0));
     ev[h] >>= 16;
     tv[h] = p.K == 1 ? f : (int)__umulhi((uint32_t)f, kinv);
   }
   __syncthreads();
 #pragma unroll
   for (int h = 0; h < PER; ++h)
-    if ((int)threadIdx.x + h * BLOCK < n) atomicOr(&mask[ev[h]], 1ull << tv[h]);
+    if ((int)threadIdx.x + h * THREADS < n) atomicOr(&mask[ev[h]], 1ull << tv[h]);
   __syncthreads();
-  for (int i = threadIdx.x; i < p.e_out; i += BLOCK) {
+  for (int i = threadIdx.x; i < p.e_out; i += THREADS) {
     const int c = __popcll(mask[i]);
     offs[i] = c;
     counts[i] = c;
   }
   __syncthreads();
-  block_exclusive_scan(offs, p.e_out, offs, wave_tot);  // in place: reads precede writes
-  for (int i = threadIdx.x; i <= p.e_out; i += BLOCK) offsets[i] = offs[i];
+  block_exclusive_scan<THREADS>(offs, p.e_out, offs, wave_tot);  // in place: reads precede writes
+  for (int i = threadIdx.x; i <= p.e_out; i += THREADS) offsets[i] = offs[i];
   // LDS reads for every slot (clamped entries are valid ids), stores for
   // the real entries
 #pragma unroll
   for (int h = 0; h < PER; ++h) {
-    const int f = threadIdx.x + h * BLOCK;
+    const int f = threadIdx.x + h * THREADS;
     const int pos = offs[ev[h]] + __popcll(mask[ev[h]] & ((1ull << tv[h]) - 1ull));
     if (f < n) {
       perm[pos] = f;
       if (inv) inv[f] = pos;
     }
   }
-  if (threadIdx.x == 0) *ticket = 0u;  // leave the control block zeroed
+  if (nroute > 1 && threadIdx.x == 0) *ticket = 0u;  // leave the control block zeroed
 }
 
 // ---------------------------------------------------------------------------
@@ -713,11 +731,20 @@ static hipError_t launch_route(const float *logits, const float *bias, int T, co
       qa.hidden ? (int)((qa.nchunks + QUANT_CHUNKS_PER_BLOCK - 1) / QUANT_CHUNKS_PER_BLOCK) : 0;
   if (T <= MOE_ROUTE_MAX_FUSED_TOKENS) {
     // one launch: routing blocks, then the quantisation blocks
-    const int grid = (T > 0 ? (T + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK : 1) + qblocks;
-    hipExtLaunchKernelGGL(route_decode_kernel<NP, LPG>, dim3(grid), dim3(BLOCK), 0, st,
-                          g_ev_before, g_ev_after, 0, logits, bias, T, rp, o->topk_ids,
-                          o->topk_weights, o->packed, o->counts, o->offsets, o->perm,
-                          o->inv_perm, reinterpret_cast<uint32_t *>(ws), qa);
+    auto launch = [&](auto kernel, int nw) {
+      const int threads = 64 * nw;
+      const int qb =
+          qa.hidden ? (int)((qa.nchunks + threads - 1) / threads) : 0;
+      const int grid = (T > 0 ? (T + nw - 1) / nw : 1) + qb;
+      hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, st, g_ev_before, g_ev_after, 0,
+                            logits, bias, T, rp, o->topk_ids, o->topk_weights, o->packed,
+                            o->counts, o->offsets, o->perm, o->inv_perm,
+                            reinterpret_cast<uint32_t *>(ws), qa);
+    };
+    if (T <= DECODE_ONE_BLOCK_WAVES)
+      launch(route_decode_kernel<NP, LPG, DECODE_ONE_BLOCK_WAVES>, DECODE_ONE_BLOCK_WAVES);
+    else
+      launch(route_decode_kernel<NP, LPG, WAVES_PER_BLOCK>, WAVES_PER_BLOCK);
     return hipGetLastError();
   }
   if (qblocks > 0) mx_quant_kernel<<<qblocks, BLOCK, 0, st>>>(qa);
