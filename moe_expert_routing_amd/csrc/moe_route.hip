@@ -242,6 +242,8 @@ __global__ __launch_bounds__(64 * NW) void route_decode_kernel(
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
     int32_t *__restrict__ inv, uint32_t *__restrict__ ticket, QuantArgs qa) {
   constexpr int THREADS = 64 * NW;
+  // the one-block kernel is launched for T <= NW only
+  constexpr bool MULTI = NW != DECODE_ONE_BLOCK_WAVES;
   const int nroute = T > 0 ? (T + NW - 1) / NW : 1;
   if ((int)blockIdx.x >= nroute) {
     mx_quant_chunk(qa, (int64_t)(blockIdx.x - nroute) * THREADS + threadIdx.x);
@@ -260,16 +262,22 @@ __global__ __launch_bounds__(64 * NW) void route_decode_kernel(
     float b[2 * NP], x[2 * NP];
     load_lane_layout<NP, LPG>(row, p, lane, x);
     load_lane_layout<NP, LPG>(bias, p, lane, b);
-    route_token<NP, LPG>(row, x, b, bias, p, lane, t, &scratch[wave], ids, wts, packed);
+    const int idp =
+        route_token<NP, LPG>(row, x, b, bias, p, lane, t, &scratch[wave], ids, wts, packed);
+    // the last block reads the output ids from a device-coherent copy, kept
+    // in perm until it writes the permutation there
+    if (MULTI && nroute > 1 && lane < p.K)
+      __hip_atomic_store(&perm[t * p.K + lane], idp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (nroute > 1) {
-    // Publish this block's outputs, then take a ticket.
-    __threadfence();
+  if (MULTI && nroute > 1) {
+    // every coherent store of the block completed, then a ticket
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (threadIdx.x == 0) is_last = (atomicAdd(ticket, 1u) == (uint32_t)nroute - 1u);
+    if (threadIdx.x == 0)
+      is_last = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                (uint32_t)nroute - 1u;
     __syncthreads();
     if (!is_last) return;
-    __threadfence();
   } else {
     __syncthreads();  // the only routing block: its own outputs, nothing to wait for
   }
@@ -286,13 +294,19 @@ __global__ __launch_bounds__(64 * NW) void route_decode_kernel(
   for (int h = 0; h < PER; ++h) ev[h] = 0;
   if (n > 0) {
 #pragma unroll
-    for (int h = 0; h < PER; ++h) ev[h] = packed[min((int)threadIdx.x + h * THREADS, n - 1)];
+    for (int h = 0; h < PER; ++h) {
+      const int f = min((int)threadIdx.x + h * THREADS, n - 1);
+      ev[h] = (MULTI && nroute > 1)
+                  ? __hip_atomic_load(&perm[f], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                  : packed[f] >> 16;
+    }
   }
+  // (every id is read into ev, and used, before the barriers below, so
+  // before perm is written)
   for (int i = threadIdx.x; i < p.e_out; i += THREADS) mask[i] = 0ull;
 #pragma unroll
   for (int h = 0; h < PER; ++h) {
     const int f = min((int)threadIdx.x + h * THREADS, max(n - 1, 0));
-    ev[h] >>= 16;
     tv[h] = p.K == 1 ? f : (int)__umulhi((uint32_t)f, kinv);
   }
   __syncthreads();
@@ -319,7 +333,7 @@ __global__ __launch_bounds__(64 * NW) void route_decode_kernel(
       if (inv) inv[f] = pos;
     }
   }
-  if (nroute > 1 && threadIdx.x == 0) *ticket = 0u;  // leave the control block zeroed
+  if (MULTI && nroute > 1 && threadIdx.x == 0) *ticket = 0u;  // leave the control block zeroed
 }
 
 // ---------------------------------------------------------------------------
