@@ -253,6 +253,7 @@ __global__ __launch_bounds__(64 * NW) void route_decode_kernel(
   __shared__ int32_t offs[MOE_ROUTE_MAX_EXPERTS + 1];
   __shared__ int32_t wave_tot[NW];
   __shared__ WaveScratch scratch[NW];
+  __shared__ int32_t own_ids[MULTI ? 1 : DECODE_ONE_BLOCK_WAVES * MOE_ROUTE_MAX_TOPK];
   __shared__ int is_last;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -268,6 +269,7 @@ __global__ __launch_bounds__(64 * NW) void route_decode_kernel(
     // in perm until it writes the permutation there
     if (MULTI && nroute > 1 && lane < p.K)
       __hip_atomic_store(&perm[t * p.K + lane], idp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!MULTI && lane < p.K) own_ids[t * p.K + lane] = idp;  // the one block's ids, in LDS
   }
   if (MULTI && nroute > 1) {
     // every coherent store of the block completed, then a ticket
@@ -296,9 +298,11 @@ __global__ __launch_bounds__(64 * NW) void route_decode_kernel(
 #pragma unroll
     for (int h = 0; h < PER; ++h) {
       const int f = min((int)threadIdx.x + h * THREADS, n - 1);
-      ev[h] = (MULTI && nroute > 1)
-                  ? __hip_atomic_load(&perm[f], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                  : packed[f] >> 16;
+      if constexpr (MULTI)
+        ev[h] = nroute > 1 ? __hip_atomic_load(&perm[f], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                           : packed[f] >> 16;
+      else
+        ev[h] = own_ids[f];
     }
   }
   // (every id is read into ev, and used, before the barriers below, so
