@@ -126,6 +126,15 @@ __device__ void block_exclusive_scan(const int32_t *in, int n, int32_t *out, int
 // every value, so the workspace needs no initial contents. A block covers at
 // most 32 tokens (32-bit token masks in LDS).
 // ---------------------------------------------------------------------------
+// Column of route block blk in its id's row of hist (rows of 8 * ceil(nblk
+// / 8) words). The hardware sends block b to XCD b % 8, so the columns of one
+// XCD's blocks are contiguous: every 64-byte line of a row is written by the
+// blocks of one XCD, through one L2, and leaves it whole.
+__device__ __forceinline__ int hist_col(int blk, int nblk) {
+  return (blk & 7) * ((nblk + 7) >> 3) + (blk >> 3);
+}
+__host__ __device__ __forceinline__ int hist_stride(int nblk) { return ((nblk + 7) >> 3) << 3; }
+
 template <int THREADS>
 __device__ void block_counts(const int32_t *__restrict__ packed, int K, int e_out, int64_t t_begin,
                              int ntok, int blk, int nblk, int32_t *__restrict__ hist,
@@ -157,7 +166,8 @@ __device__ void block_counts(const int32_t *__restrict__ packed, int K, int e_ou
     const int i = tid + h * THREADS;
     if (i < n) rank8[t_begin * K + i] = (uint8_t)__popc(lds_mask[ev[h]] & ((1u << tv[h]) - 1u));
   }
-  for (int e = tid; e < e_out; e += THREADS) hist[(size_t)e * nblk + blk] = __popc(lds_mask[e]);
+  const int col = hist_col(blk, nblk), stride = hist_stride(nblk);
+  for (int e = tid; e < e_out; e += THREADS) hist[(size_t)e * stride + col] = __popc(lds_mask[e]);
 }
 
 // ---------------------------------------------------------------------------
@@ -438,7 +448,7 @@ constexpr int SCAN_PER_THREAD = 8;
 __global__ __launch_bounds__(BLOCK) void block_prefix_kernel(int32_t *__restrict__ hist, int nblk,
                                                              int32_t *__restrict__ counts) {
   __shared__ int32_t wave_tot[WAVES_PER_BLOCK];
-  int32_t *row = hist + (size_t)blockIdx.x * nblk;
+  int32_t *row = hist + (size_t)blockIdx.x * hist_stride(nblk);  // block t at row[hist_col(t)]
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   int carry = 0;
   for (int base = 0; base < nblk; base += BLOCK * SCAN_PER_THREAD) {
@@ -447,7 +457,7 @@ __global__ __launch_bounds__(BLOCK) void block_prefix_kernel(int32_t *__restrict
     int sum = 0;
 #pragma unroll
     for (int k = 0; k < SCAN_PER_THREAD; ++k) {
-      v[k] = (beg + k < nblk) ? row[beg + k] : 0;
+      v[k] = (beg + k < nblk) ? row[hist_col(beg + k, nblk)] : 0;
       sum += v[k];
     }
     const int incl = wave_inclusive_scan(sum);
@@ -462,7 +472,7 @@ __global__ __launch_bounds__(BLOCK) void block_prefix_kernel(int32_t *__restrict
     int run = off + incl - sum;
 #pragma unroll
     for (int k = 0; k < SCAN_PER_THREAD; ++k) {
-      if (beg + k < nblk) row[beg + k] = run;
+      if (beg + k < nblk) row[hist_col(beg + k, nblk)] = run;
       run += v[k];
     }
     carry += total;
@@ -500,7 +510,9 @@ __global__ __launch_bounds__(BLOCK) void scatter_kernel(
 #pragma unroll
   for (int k = 0; k < SCATTER_PER_THREAD; ++k) {
     const int64_t f = f0 + (int64_t)k * BLOCK;
-    hv[k] = f < n ? hist[(size_t)ev[k] * nblk + (int)((f / K) / tokens_per_blk)] : 0;
+    hv[k] = f < n ? hist[(size_t)ev[k] * hist_stride(nblk) +
+                         hist_col((int)((f / K) / tokens_per_blk), nblk)]
+                  : 0;
   }
   scan_store(cv, e_out, offs, wave_tot);
   if (blockIdx.x == 0)
@@ -727,7 +739,7 @@ static size_t route_ws_bytes(int T, int e_out, int K) {
   size_t b = CONTROL_BYTES;
   if (T > MOE_ROUTE_MAX_FUSED_TOKENS) {
     const size_t nblk = ((size_t)T + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK;
-    b += align256(nblk * e_out * sizeof(int32_t));  // hist
+    b += align256((size_t)hist_stride((int)nblk) * e_out * sizeof(int32_t));  // hist
     b += align256((size_t)T * K);                    // rank8
   }
   return b;
@@ -771,8 +783,8 @@ static hipError_t launch_route(const float *logits, const float *bias, int T, co
   const int nblk = (T + tpb - 1) / tpb;
   PrefillCounts pc;
   pc.hist = reinterpret_cast<int32_t *>(ws + CONTROL_BYTES);
-  pc.rank8 = reinterpret_cast<uint8_t *>(ws + CONTROL_BYTES +
-                                         align256((size_t)nblk * rp.e_out * sizeof(int32_t)));
+  pc.rank8 = reinterpret_cast<uint8_t *>(
+      ws + CONTROL_BYTES + align256((size_t)hist_stride(nblk) * rp.e_out * sizeof(int32_t)));
   // the benchmark hook's events are recorded by the launch itself
   if (rows_path) {
     hipExtLaunchKernelGGL(route_rows_kernel, dim3(nblk), dim3(ROWS_BLOCK), 0, st, g_ev_before,
