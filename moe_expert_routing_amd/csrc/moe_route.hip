@@ -495,7 +495,11 @@ __global__ __launch_bounds__(BLOCK) void scatter_kernel(
     int32_t *__restrict__ perm, int32_t *__restrict__ inv) {
   __shared__ int32_t offs[MOE_ROUTE_MAX_EXPERTS + 1];
   __shared__ int32_t wave_tot[WAVES_PER_BLOCK];
-  const int64_t f0 = (int64_t)blockIdx.x * BLOCK * SCATTER_PER_THREAD + threadIdx.x;
+  // consecutive entry chunks go to blocks on one XCD (block b runs on XCD
+  // b % 8), so the perm lines they share are written through one L2
+  const int nb = (int)gridDim.x, b = (int)blockIdx.x;
+  const int chunk = (nb % 8 == 0) ? (b % 8) * (nb / 8) + b / 8 : b;
+  const int64_t f0 = (int64_t)chunk * BLOCK * SCATTER_PER_THREAD + threadIdx.x;
   // counts first: the offsets scan then overlaps the entry loads
   int cv[4];
   scan_load(counts, e_out, cv);
