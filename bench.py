@@ -298,6 +298,22 @@ def main():
         decode_quant[f"T{Td}"] = round(time_calls(qfn, args.decode_calls), 2)
         decode_quant_graph[f"T{Td}"] = round(time_graph(qfn, args.decode_calls), 2)
 
+    # the decode sweep (5..64 tokens, rank range [336, 448) -> 128 local ids,
+    # exact twins among the logits): us per call from a HIP graph
+    decode_sweep_graph = {}
+    for Td in W.DECODE_SWEEP_T:
+        c = W.decode_sweep(Td, 3)
+        log(f"bench: decode sweep T={Td}")
+        dl = torch.from_numpy(c.logits).to(dev)
+        db = torch.from_numpy(c.bias).to(dev)
+        eo = M.local_num_experts(W.E, W.K, c.off, c.cnt) or W.E
+        sout = M.alloc_outputs(Td, W.K, eo, dev)
+        sws = torch.zeros(1 << 16, dtype=torch.uint8, device=dev)
+        sfn = (lambda dl=dl, db=db, c=c, sout=sout, sws=sws:
+               M.route_local(dl, db, c.off, c.cnt, out=sout, ws=sws))
+        sfn()
+        decode_sweep_graph[f"T{Td}"] = round(time_graph(sfn, args.decode_calls), 2)
+
     # ------------------------------------------------------------------
     # grouped-GEMM layout of the long-prefill step's entries (tile 128): us
     # per call (eager and replayed from a HIP graph) and GB/s over its
@@ -406,6 +422,7 @@ def main():
         "decode_us_per_call": decode,
         "empty_kernel_us_per_call": floor,
         "decode_us_per_call_hipgraph": decode_graph,
+        "decode_sweep_rank_local_us_per_call_hipgraph": decode_sweep_graph,
         "router_gemm_route": gemm,
         "grouped_layout_32768": grouped,
         "balance_plan_32768": balance,
