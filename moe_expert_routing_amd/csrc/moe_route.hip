@@ -239,9 +239,14 @@ __global__ __launch_bounds__(BLOCK) void mx_quant_kernel(QuantArgs qa) {
 // ---------------------------------------------------------------------------
 // Decode path: one launch for T <= 64, NW waves (one token each) per block.
 // With one routing block (T <= NW) the block builds the permutation right
-// after its own barrier; with several, every block publishes its outputs,
-// fences and takes a ticket, and the last one builds it. Blocks past the
-// routing blocks quantise the activations.
+// after its own barrier, from its output ids kept in LDS. With several, every
+// block also writes its output ids into perm with device-scope (coherent)
+// stores, waits for them to complete and takes a ticket with a device-scope
+// atomic; the last block reads the ids back with device-scope loads and
+// builds the permutation over them. Nothing else it reads was written by
+// another block of the launch, so no device-wide fence (L2 write-back or
+// invalidate) is needed. Blocks past the routing blocks quantise the
+// activations.
 // ---------------------------------------------------------------------------
 constexpr int DECODE_ONE_BLOCK_WAVES = 8;  // T <= 8: one routing block
 
