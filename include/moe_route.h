@@ -111,6 +111,7 @@ size_t moe_route_workspace_bytes(int32_t num_tokens, int32_t num_experts_out,
  *   logits   [T, E] fp32 router logits
  *   bias     [E]    fp32 correction bias (added for selection only)
  * Writes every buffer of `out`. T = 0 writes zero counts and offsets.
+ * T * top_k above 2^31 - 1 -> MOE_ERR_SHAPE (entries and positions are int32).
  * Returns MOE_OK or a negative moe_status.
  */
 int moe_route(const float *logits, const float *bias, int32_t num_tokens,

@@ -492,6 +492,7 @@ __global__ __launch_bounds__(BLOCK) void block_prefix_kernel(int32_t *__restrict
 // SCATTER_PER_THREAD entries and issues each round of loads for all of them
 // before using any.
 constexpr int SCATTER_PER_THREAD = 4;
+constexpr int SCATTER_TAB = 2048;  // LDS words for the chunk's route-block prefixes
 
 __global__ __launch_bounds__(BLOCK) void scatter_kernel(
     const int32_t *__restrict__ packed, const int32_t *__restrict__ hist,
@@ -500,38 +501,74 @@ __global__ __launch_bounds__(BLOCK) void scatter_kernel(
     int32_t *__restrict__ perm, int32_t *__restrict__ inv) {
   __shared__ int32_t offs[MOE_ROUTE_MAX_EXPERTS + 1];
   __shared__ int32_t wave_tot[WAVES_PER_BLOCK];
+  __shared__ int32_t tab[SCATTER_TAB];
   // consecutive entry chunks go to blocks on one XCD (block b runs on XCD
   // b % 8), so the perm lines they share are written through one L2
   const int nb = (int)gridDim.x, b = (int)blockIdx.x;
   const int chunk = (nb % 8 == 0) ? (b % 8) * (nb / 8) + b / 8 : b;
-  const int64_t f0 = (int64_t)chunk * BLOCK * SCATTER_PER_THREAD + threadIdx.x;
-  // counts first: the offsets scan then overlaps the entry loads
-  int cv[4];
-  scan_load(counts, e_out, cv);
+  // entry indices fit in 32 bits (n < 2^31, checked on the host); an entry's
+  // route block is f / (K * tokens_per_blk)
+  const int nn = (int)n;
+  const uint32_t kt = (uint32_t)(K * tokens_per_blk);
+  const int fb = chunk * BLOCK * SCATTER_PER_THREAD;  // the chunk's first entry (< n)
+  const int fe = min(fb + BLOCK * SCATTER_PER_THREAD, nn) - 1;
+  // the route blocks the chunk spans; when their prefixes for every id fit
+  // in LDS they are loaded together with the entries (one round trip),
+  // otherwise each entry's prefix is read after its id
+  const int rb0 = (int)((uint32_t)fb / kt);
+  const int nrb = (int)((uint32_t)fe / kt) - rb0 + 1;
+  const bool tabled = nrb * e_out <= SCATTER_TAB;  // block-uniform
+  const int stride = hist_stride(nblk);
+  // Every load of the first round (counts, the entries, the table) is issued
+  // before any is used: clamped indices, no branches between them.
+  int cx[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) cx[k] = counts[min((int)threadIdx.x * 4 + k, e_out - 1)];
   int ev[SCATTER_PER_THREAD], rv[SCATTER_PER_THREAD];
 #pragma unroll
   for (int k = 0; k < SCATTER_PER_THREAD; ++k) {
-    const int64_t f = f0 + (int64_t)k * BLOCK;
-    ev[k] = f < n ? packed[f] >> 16 : 0;
-    rv[k] = f < n ? rank8[f] : 0;
+    const int f = min(fb + (int)threadIdx.x + k * BLOCK, fe);
+    ev[k] = packed[f];
+    rv[k] = rank8[f];
   }
+  constexpr int TAB_PER = SCATTER_TAB / BLOCK;
+  // (loaded whether or not the table is used: in-range entries either way)
+  const int ntab = min(nrb * e_out, SCATTER_TAB);
+  int tv[TAB_PER];
+#pragma unroll
+  for (int h = 0; h < TAB_PER; ++h) {
+    const int i = min((int)threadIdx.x + h * BLOCK, ntab - 1);
+    const int rb = i / e_out;  // (route block rb0 + rb, id i - rb e_out)
+    tv[h] = hist[(size_t)(i - rb * e_out) * stride + hist_col(rb0 + rb, nblk)];
+  }
+  int cv[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) cv[k] = ((int)threadIdx.x * 4 + k < e_out) ? cx[k] : 0;
+#pragma unroll
+  for (int k = 0; k < SCATTER_PER_THREAD; ++k) ev[k] >>= 16;
+#pragma unroll
+  for (int h = 0; h < TAB_PER; ++h)
+    if ((int)threadIdx.x + h * BLOCK < ntab) tab[threadIdx.x + h * BLOCK] = tv[h];
   int hv[SCATTER_PER_THREAD];
 #pragma unroll
-  for (int k = 0; k < SCATTER_PER_THREAD; ++k) {
-    const int64_t f = f0 + (int64_t)k * BLOCK;
-    hv[k] = f < n ? hist[(size_t)ev[k] * hist_stride(nblk) +
-                         hist_col((int)((f / K) / tokens_per_blk), nblk)]
-                  : 0;
+  for (int k = 0; k < SCATTER_PER_THREAD; ++k) hv[k] = 0;
+  if (!tabled) {
+#pragma unroll
+    for (int k = 0; k < SCATTER_PER_THREAD; ++k) {
+      const int f = min(fb + (int)threadIdx.x + k * BLOCK, fe);
+      hv[k] = hist[(size_t)ev[k] * stride + hist_col((int)((uint32_t)f / kt), nblk)];
+    }
   }
-  scan_store(cv, e_out, offs, wave_tot);
+  scan_store(cv, e_out, offs, wave_tot);  // its barriers also publish tab
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i <= e_out; i += BLOCK) offsets[i] = offs[i];
 #pragma unroll
   for (int k = 0; k < SCATTER_PER_THREAD; ++k) {
-    const int64_t f = f0 + (int64_t)k * BLOCK;
-    if (f < n) {
-      const int32_t pos = offs[ev[k]] + hv[k] + rv[k];
-      perm[pos] = (int32_t)f;
+    const int f = fb + (int)threadIdx.x + k * BLOCK;
+    if (f <= fe) {
+      const int h = tabled ? tab[((int)((uint32_t)f / kt) - rb0) * e_out + ev[k]] : hv[k];
+      const int32_t pos = offs[ev[k]] + h + rv[k];
+      perm[pos] = f;
       if (inv) inv[f] = pos;
     }
   }
@@ -820,6 +857,8 @@ int validate_route_call(const float *logits, const float *bias, int32_t T,
   if (st != MOE_OK) return st;
   if (!o) return MOE_ERR_NULL;
   if (T < 0) return MOE_ERR_SHAPE;
+  // entries f = t * top_k + k and their positions are int32
+  if ((int64_t)T * prm->top_k > (int64_t)INT32_MAX) return MOE_ERR_SHAPE;
   if (!o->counts || !o->offsets) return MOE_ERR_NULL;
   if (T > 0 && (!logits || !bias || !o->topk_ids || !o->topk_weights || !o->packed || !o->perm))
     return MOE_ERR_NULL;
