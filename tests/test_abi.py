@@ -115,6 +115,9 @@ def test_null_and_shape_validation(L):
     assert _route_local(L, prm, off=890, cnt=10) == ERR_RANGE
     assert _route_local(L, prm, off=-1, cnt=4) == ERR_RANGE
     assert _route_local(L, prm, logits=FAKE + 4) == ERR_SHAPE  # misaligned rows
+    # entries t * top_k + k and their positions are int32: 2^27 tokens x 16
+    assert _route_local(L, prm, T=1 << 27, ws_bytes=1 << 62) == ERR_SHAPE
+    assert _route_local(L, prm, T=(1 << 27) - 1, ws_bytes=1 << 20) == ERR_WS
     assert L.moe_route(FAKE, FAKE, 8, None, ctypes.byref(_outs()), FAKE, 1 << 20, None) == ERR_NULL
 
 
