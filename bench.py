@@ -59,6 +59,18 @@ def parse():
     return ap.parse_args()
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (Linux), or an empty string."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
 def source_digest() -> str:
     """Digest of the routing sources' code: comments and blank space are
     dropped first, so that a documentation edit does not retire a profile
@@ -395,7 +407,7 @@ def main():
                "sample": f"first {done} of the {T} long-prefill tokens, routed in chunks of "
                          f"{chunk} tokens (each chunk a full oracle call incl. permutation), "
                          f"{el:.1f} s single-threaded Python+numpy on "
-                         f"{platform.processor() or platform.machine()}, "
+                         f"{cpu_model() or platform.processor() or platform.machine()}, "
                          f"{os.cpu_count()} host cores present"}
 
     frac = kern_gbps / HBM_PEAK_GBPS
