@@ -131,18 +131,38 @@ def _stream_handle(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-_WORKSPACES: Dict[int, torch.Tensor] = {}
+# Default workspaces, one per (device, stream): calls that may run at the same
+# time must not share one (the decode ticket and the prefill tile counts live
+# there), and a workspace is only ever replaced on the stream it was
+# allocated and used on, so the caching allocator's stream tracking holds.
+_WORKSPACES: Dict[tuple, torch.Tensor] = {}
 
 
-def workspace(device: torch.device, nbytes: int) -> torch.Tensor:
-    """A zero-initialised byte buffer of at least nbytes, cached per device.
-    Its control block is zero when allocated and every call leaves it zero."""
+def _new_workspace(nbytes: int, device: torch.device) -> torch.Tensor:
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+
+def workspace(device: torch.device, nbytes: int, stream: Optional[int] = None) -> torch.Tensor:
+    """A zero-initialised byte buffer of at least nbytes, cached per (device,
+    stream); `stream` defaults to the device's current stream. Its control
+    block is zero when allocated and every call leaves it zero."""
     idx = device.index if device.index is not None else torch.cuda.current_device()
-    ws = _WORKSPACES.get(idx)
+    if stream is None:
+        stream = _stream_handle(torch.device("cuda", idx))
+    key = (idx, int(stream))
+    ws = _WORKSPACES.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 1 << 16), dtype=torch.uint8, device=device)
-        _WORKSPACES[idx] = ws
+        ws = _new_workspace(max(nbytes, 1 << 16), device)
+        _WORKSPACES[key] = ws
     return ws
+
+
+def cached_workspace(device: torch.device, stream: Optional[int] = None):
+    """The default workspace of (device, stream) if one was made, else None."""
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    if stream is None:
+        stream = _stream_handle(torch.device("cuda", idx))
+    return _WORKSPACES.get((idx, int(stream)))
 
 
 def alloc_outputs(T: int, top_k: int, e_out: int, device: torch.device,
@@ -207,13 +227,14 @@ def route_local(logits: torch.Tensor, bias: torch.Tensor, local_expert_offset: i
     dev = logits.device
     if out is None:
         out = alloc_outputs(T, top_k, e_out, dev)
+    sh = _stream_handle(dev)
     if ws is None:  # a caller's workspace is checked by the library itself
-        ws = workspace(dev, lib().moe_route_workspace_bytes(T, e_out, top_k))
+        ws = workspace(dev, lib().moe_route_workspace_bytes(T, e_out, top_k), sh)
     prm = _params_ref(E, n_groups, topk_group, top_k, group_topn)
     o = _outputs_struct(out)
     st = lib().moe_route_local(logits.data_ptr(), bias.data_ptr(), T, prm[1],
                                local_expert_offset, num_local_experts, ctypes.byref(o),
-                               ws.data_ptr(), ws.numel(), _stream_handle(dev))
+                               ws.data_ptr(), ws.numel(), sh)
     if st:
         _check(st, "moe_route_local")
     out["num_experts_out"] = e_out
@@ -245,15 +266,15 @@ def route_quant_local(logits: torch.Tensor, bias: torch.Tensor, hidden: torch.Te
     if "act_q" not in out:
         out["act_q"] = torch.empty((T, H), dtype=torch.uint8, device=dev)
         out["act_scale"] = torch.empty((T, H // 32), dtype=torch.uint8, device=dev)
+    sh = _stream_handle(dev)
     if ws is None:
-        ws = workspace(dev, lib().moe_route_workspace_bytes(T, e_out, top_k))
+        ws = workspace(dev, lib().moe_route_workspace_bytes(T, e_out, top_k), sh)
     prm = _params_ref(E, n_groups, topk_group, top_k, group_topn)
     o = _outputs_struct(out)
     st = lib().moe_route_quant_local(logits.data_ptr(), bias.data_ptr(), T, prm[1],
                                      local_expert_offset, num_local_experts, hidden.data_ptr(),
                                      H, out["act_q"].data_ptr(), out["act_scale"].data_ptr(),
-                                     ctypes.byref(o), ws.data_ptr(), ws.numel(),
-                                     _stream_handle(dev))
+                                     ctypes.byref(o), ws.data_ptr(), ws.numel(), sh)
     if st:
         _check(st, "moe_route_quant_local")
     out["num_experts_out"] = e_out
@@ -270,12 +291,13 @@ def route(logits: torch.Tensor, bias: torch.Tensor, *, n_groups: int = 8, topk_g
     dev = logits.device
     if out is None:
         out = alloc_outputs(T, top_k, E, dev)
+    sh = _stream_handle(dev)
     if ws is None:  # a caller's workspace is checked by the library itself
-        ws = workspace(dev, lib().moe_route_workspace_bytes(T, E, top_k))
+        ws = workspace(dev, lib().moe_route_workspace_bytes(T, E, top_k), sh)
     prm = _params_ref(E, n_groups, topk_group, top_k, group_topn)
     o = _outputs_struct(out)
     st = lib().moe_route(logits.data_ptr(), bias.data_ptr(), T, prm[1], ctypes.byref(o),
-                         ws.data_ptr(), ws.numel(), _stream_handle(dev))
+                         ws.data_ptr(), ws.numel(), sh)
     _check(st, "moe_route")
     out["num_experts_out"] = E
     return out
@@ -307,14 +329,15 @@ def router_gemm_route(hidden: torch.Tensor, weight: torch.Tensor, bias: torch.Te
     if out is None:
         out = alloc_outputs(T, top_k, e_out, dev)
     need = lib().moe_router_gemm_route_workspace_bytes(T, H, E, e_out, top_k)
+    sh = _stream_handle(dev)
     if ws is None:
-        ws = workspace(dev, need)
+        ws = workspace(dev, need, sh)
     prm = _params(E, n_groups, topk_group, top_k, group_topn)
     o = _outputs_struct(out)
     st = lib().moe_router_gemm_route(hidden.data_ptr(), weight.data_ptr(), T, H,
                                       bias.data_ptr(), logits.data_ptr(), ctypes.byref(prm),
                                       local_expert_offset, num_local_experts, ctypes.byref(o),
-                                      ws.data_ptr(), ws.numel(), _stream_handle(dev))
+                                      ws.data_ptr(), ws.numel(), sh)
     _check(st, "moe_router_gemm_route")
     out["logits"] = logits
     out["num_experts_out"] = e_out

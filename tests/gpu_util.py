@@ -37,7 +37,8 @@ def run_case(case, check_ws=True):
 
 def assert_workspace_zero():
     """Every call must leave the workspace's control block zeroed."""
-    ws = M._WORKSPACES[DEV.index or 0]
+    ws = M.cached_workspace(DEV)
+    assert ws is not None, "no default workspace on the current stream"
     assert int(ws[:256].count_nonzero()) == 0, "control block not left zeroed"
 
 
