@@ -126,14 +126,21 @@ __device__ void block_exclusive_scan(const int32_t *in, int n, int32_t *out, int
 // every value, so the workspace needs no initial contents. A block covers at
 // most 32 tokens (32-bit token masks in LDS).
 // ---------------------------------------------------------------------------
-// Column of route block blk in its id's row of hist (rows of 8 * ceil(nblk
-// / 8) words). The hardware sends block b to XCD b % 8, so the columns of one
-// XCD's blocks are contiguous: every 64-byte line of a row is written by the
-// blocks of one XCD, through one L2, and leaves it whole.
-__device__ __forceinline__ int hist_col(int blk, int nblk) {
-  return (blk & 7) * ((nblk + 7) >> 3) + (blk >> 3);
+// Column of count tile `tile` in its id's row of hist. Count tiles are the
+// token groups that one route block counts together; a route block covers
+// 2^lg consecutive tiles. The hardware sends route block b to XCD b % 8, so
+// the columns of one XCD's blocks are made contiguous: every 64-byte line of
+// a row is written by the blocks of one XCD, through one L2, and leaves it
+// whole. Rows are hist_stride(ntiles, lg) words long.
+__host__ __device__ __forceinline__ int hist_stride(int ntiles, int lg = 0) {
+  const int nb = (ntiles + (1 << lg) - 1) >> lg;
+  return ((nb + 7) >> 3) << (3 + lg);
 }
-__host__ __device__ __forceinline__ int hist_stride(int nblk) { return ((nblk + 7) >> 3) << 3; }
+__device__ __forceinline__ int hist_col(int tile, int ntiles, int lg = 0) {
+  const int b = tile >> lg, i = tile & ((1 << lg) - 1);
+  const int nb = (ntiles + (1 << lg) - 1) >> lg;
+  return ((((b & 7) * ((nb + 7) >> 3)) + (b >> 3)) << lg) + i;
+}
 
 template <int THREADS>
 __device__ void block_counts(const int32_t *__restrict__ packed, int K, int e_out, int64_t t_begin,
@@ -390,59 +397,128 @@ __global__ __launch_bounds__(BLOCK) void route_tokens_kernel(
 }
 
 // Prefill path, kernel 1 for the 896-expert, 8-group shape: four tokens per
-// wave (route_rows.hpp); rows that fail their certificate are routed again
-// one token per wave. Then the block's share of the tile counts.
+// wave (route_rows.hpp), two count tiles of 16 tokens per block, software-
+// pipelined in every wave: the first pass of the wave's next tile is
+// requested before the current tile's selection runs, so the selection of
+// one tile overlaps the memory latency of the next (the whole grid no longer
+// streams first and selects last). Rows that fail their certificate are
+// routed again one token per wave. Then each tile's counts.
 __device__ unsigned long long g_row_fallback_tokens = 0ull;
 
 constexpr int ROWS_WAVES = 4;
 constexpr int ROWS_BLOCK = 64 * ROWS_WAVES;
-constexpr int ROWS_TOKENS_PER_BLOCK = 4 * ROWS_WAVES;
-static_assert(ROWS_TOKENS_PER_BLOCK <= 32 && WAVES_PER_BLOCK <= 32, "32-bit token masks");
+constexpr int ROWS_TILE_TOKENS = 4 * ROWS_WAVES;  // tokens per count tile
+constexpr int ROWS_TILES_LG = 1;                  // 2 tiles per block
+constexpr int ROWS_TILES = 1 << ROWS_TILES_LG;
+constexpr int ROWS_TOKENS_PER_BLOCK = ROWS_TILE_TOKENS * ROWS_TILES;
+static_assert(ROWS_TILE_TOKENS <= 32 && WAVES_PER_BLOCK <= 32, "32-bit token masks");
+static_assert(ROWS_TILE_TOKENS * rows::MAX_K <= ROWS_BLOCK, "one entry per thread");
 
-__global__ __launch_bounds__(ROWS_BLOCK, 8) void route_rows_kernel(
+struct RowsLds {
+  rows::RowScratch wave[ROWS_WAVES];
+  int32_t ids[ROWS_TILES][ROWS_WAVES][4][rows::MAX_K];  // output ids by tile, wave, row, slot
+};
+
+// The wave's rows of its tiles (tile i: tokens tb + 16 i + 4 wave + r), in
+// key window W. Returns 4 bits per tile of rows to route again.
+template <int W>
+__device__ __forceinline__ uint32_t route_tiles(const float *__restrict__ logits,
+                                                const float *__restrict__ bias,
+                                                const float *__restrict__ bias_lds, int T,
+                                                int64_t tb, int wave, const RouteParams &p,
+                                                int lane, RowsLds &L, int32_t *__restrict__ ids,
+                                                float *__restrict__ wts,
+                                                int32_t *__restrict__ packed) {
+  const int r = lane >> 4, c = (lane & 15) >> 2, sub = lane & 3;
+  auto tile_t0 = [&](int i) { return tb + (int64_t)ROWS_TILE_TOKENS * i + 4 * wave; };
+  auto row_of = [&](int i) {
+    const int64_t t = tile_t0(i) + r;
+    return logits + (size_t)(t < T ? t : (int64_t)T - 1) * rows::E;
+  };
+  uint32_t redo = 0u;
+  float4 xq[rows::PREFETCH];
+  rows::first_loads(row_of(0), c, sub, xq);
+#pragma unroll 1
+  for (int i = 0; i < ROWS_TILES; ++i) {
+    uint32_t a[rows::PP], b[rows::PP];
+    __builtin_amdgcn_s_setprio(3);
+    rows::stream_pools(row_of(i), bias_lds, c, sub, xq, a, b);
+    const bool next = i + 1 < ROWS_TILES && tile_t0(i + 1) < T;  // wave-uniform
+    if (next) rows::first_loads(row_of(i + 1), c, sub, xq);
+    __builtin_amdgcn_sched_barrier(0);
+    redo |= rows::route_rows4_post<W>(a, b, logits, bias, bias_lds, T, tile_t0(i), p, lane,
+                                      &L.wave[wave], L.ids[i][wave], ids, wts, packed)
+            << (4 * i);
+    if (!next) break;
+  }
+  return redo;
+}
+
+__global__ __launch_bounds__(ROWS_BLOCK, 4) void route_rows_kernel(
     const float *__restrict__ logits, const float *__restrict__ bias, int T, RouteParams p,
     int32_t *__restrict__ ids, float *__restrict__ wts, int32_t *__restrict__ packed,
     PrefillCounts pc) {
-  __shared__ float bias_lds[2][rows::E];  // fl32(b + B) of each key window
-  // routing scratch, reused for the tile counts once every wave is done
-  __shared__ union {
-    union {
-      rows::RowScratch r;
-      WaveScratch w;
-    } wave[ROWS_WAVES];
-    uint32_t mask[MOE_ROUTE_MAX_EXPERTS];
-  } lds;
+  __shared__ __align__(16) float bias_lds[rows::E];  // fl32(b + B) of the block's key window
+  __shared__ RowsLds L;
   __shared__ int bad_bias[ROWS_WAVES];
-  const int window = rows::stage_bias<ROWS_BLOCK>(bias, bias_lds[0], bias_lds[1], bad_bias);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int64_t tb = (int64_t)blockIdx.x * ROWS_TOKENS_PER_BLOCK;
-  const int64_t t0 = tb + 4 * wave;
-  if (t0 < T) {
-    uint32_t redo = 0xFu;
+  // the whole kernel starts at the streaming issue priority (see route_rows4_post)
+  __builtin_amdgcn_s_setprio(3);
+  const int window = rows::stage_bias<ROWS_BLOCK>(bias, bias_lds, bad_bias);
+  uint32_t redo = 0u;
+  if (tb + 4 * wave < T) {
     if (window == 0)
-      redo = rows::route_rows4<0>(logits, bias, bias_lds[0], T, t0, p, lane, &lds.wave[wave].r, ids,
-                                  wts, packed);
+      redo = route_tiles<0>(logits, bias, bias_lds, T, tb, wave, p, lane, L, ids, wts, packed);
     else if (window == 1)
-      redo = rows::route_rows4<1>(logits, bias, bias_lds[1], T, t0, p, lane, &lds.wave[wave].r, ids,
-                                  wts, packed);
-    redo = (uint32_t)__builtin_amdgcn_readfirstlane((int)redo);
-    while (redo) {
-      const int r = __builtin_ctz(redo);
-      redo &= redo - 1u;
-      const int64_t t = t0 + r;
-      if (t >= T) break;
-      if (lane == 0) atomicAdd(&g_row_fallback_tokens, 1ull);
-      const float *row = logits + (size_t)t * p.E;
-      float b[14], x[14];
-      load_lane_layout<7, 8>(row, p, lane, x);
-      load_lane_layout<7, 8>(bias, p, lane, b);
-      route_token_plain<7, 8>(row, x, b, p, lane, t, ids, wts, packed);
-    }
+      redo = route_tiles<1>(logits, bias, bias_lds, T, tb, wave, p, lane, L, ids, wts, packed);
+    else
+      redo = (1u << (4 * ROWS_TILES)) - 1u;  // a bias outside both windows
   }
-  block_counts<ROWS_BLOCK>(packed, p.K, p.e_out, tb,
-                          (int)min((int64_t)ROWS_TOKENS_PER_BLOCK, T - tb), blockIdx.x,
-                          gridDim.x, pc.hist, pc.rank8, lds.mask);
+  redo = (uint32_t)__builtin_amdgcn_readfirstlane((int)redo);
+  while (redo) {
+    const int q = __builtin_ctz(redo), i = q >> 2, r = q & 3;
+    redo &= redo - 1u;
+    const int64_t t = tb + (int64_t)ROWS_TILE_TOKENS * i + 4 * wave + r;
+    if (t >= T) continue;
+    if (lane == 0) atomicAdd(&g_row_fallback_tokens, 1ull);
+    const float *row = logits + (size_t)t * p.E;
+    float b[14], x[14];
+    load_lane_layout<7, 8>(row, p, lane, x);
+    load_lane_layout<7, 8>(bias, p, lane, b);
+    const int idp = route_token_plain<7, 8>(row, x, b, p, lane, t, ids, wts, packed);
+    if (lane < p.K) L.ids[i][wave][r][lane] = idp;
+  }
+  // Each tile's counts, from the output ids the waves left in LDS; the token
+  // masks take the bias staging's LDS, free once every wave is done
+  // (E' <= 896 words).
+  uint32_t *mask = reinterpret_cast<uint32_t *>(bias_lds);
+  const int ntiles = (T + ROWS_TILE_TOKENS - 1) / ROWS_TILE_TOKENS;
+#pragma unroll 1
+  for (int i = 0; i < ROWS_TILES; ++i) {
+    const int64_t t0 = tb + (int64_t)ROWS_TILE_TOKENS * i;
+    if (t0 >= T) break;  // block-uniform
+    __syncthreads();
+    for (int e = threadIdx.x; e < p.e_out; e += ROWS_BLOCK) mask[e] = 0u;
+    __syncthreads();
+    const int ntok = (int)min((int64_t)ROWS_TILE_TOKENS, T - t0);
+    const int n = ntok * p.K;  // <= 256 = ROWS_BLOCK
+    const int f = threadIdx.x;
+    int ev = 0, tk = 0;
+    if (f < n) {
+      tk = f / p.K;
+      ev = L.ids[i][tk >> 2][tk & 3][f - tk * p.K];
+      ev = (unsigned)ev < (unsigned)p.e_out ? ev : 0;  // (every id is in range; guard only)
+      atomicOr(&mask[ev], 1u << tk);
+    }
+    __syncthreads();
+    if (f < n) pc.rank8[t0 * p.K + f] = (uint8_t)__popc(mask[ev] & ((1u << tk) - 1u));
+    const int tile = (int)blockIdx.x * ROWS_TILES + i;
+    const int col = hist_col(tile, ntiles, ROWS_TILES_LG), stride = hist_stride(ntiles, ROWS_TILES_LG);
+    for (int e = threadIdx.x; e < p.e_out; e += ROWS_BLOCK)
+      pc.hist[(size_t)e * stride + col] = __popc(mask[e]);
+  }
 }
 
 // Prefill permutation, part 2: one block per output id: exclusive scan of
@@ -451,9 +527,9 @@ __global__ __launch_bounds__(ROWS_BLOCK, 8) void route_rows_kernel(
 constexpr int SCAN_PER_THREAD = 8;
 
 __global__ __launch_bounds__(BLOCK) void block_prefix_kernel(int32_t *__restrict__ hist, int nblk,
-                                                             int32_t *__restrict__ counts) {
+                                                             int lg, int32_t *__restrict__ counts) {
   __shared__ int32_t wave_tot[WAVES_PER_BLOCK];
-  int32_t *row = hist + (size_t)blockIdx.x * hist_stride(nblk);  // block t at row[hist_col(t)]
+  int32_t *row = hist + (size_t)blockIdx.x * hist_stride(nblk, lg);  // tile t at row[hist_col(t)]
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   int carry = 0;
   for (int base = 0; base < nblk; base += BLOCK * SCAN_PER_THREAD) {
@@ -462,7 +538,7 @@ __global__ __launch_bounds__(BLOCK) void block_prefix_kernel(int32_t *__restrict
     int sum = 0;
 #pragma unroll
     for (int k = 0; k < SCAN_PER_THREAD; ++k) {
-      v[k] = (beg + k < nblk) ? row[hist_col(beg + k, nblk)] : 0;
+      v[k] = (beg + k < nblk) ? row[hist_col(beg + k, nblk, lg)] : 0;
       sum += v[k];
     }
     const int incl = wave_inclusive_scan(sum);
@@ -477,7 +553,7 @@ __global__ __launch_bounds__(BLOCK) void block_prefix_kernel(int32_t *__restrict
     int run = off + incl - sum;
 #pragma unroll
     for (int k = 0; k < SCAN_PER_THREAD; ++k) {
-      if (beg + k < nblk) row[hist_col(beg + k, nblk)] = run;
+      if (beg + k < nblk) row[hist_col(beg + k, nblk, lg)] = run;
       run += v[k];
     }
     carry += total;
@@ -497,7 +573,7 @@ constexpr int SCATTER_TAB = 2048;  // LDS words for the chunk's route-block pref
 __global__ __launch_bounds__(BLOCK) void scatter_kernel(
     const int32_t *__restrict__ packed, const int32_t *__restrict__ hist,
     const uint8_t *__restrict__ rank8, const int32_t *__restrict__ counts, int e_out, int nblk,
-    int tokens_per_blk, int K, int64_t n, int32_t *__restrict__ offsets,
+    int lg, int tokens_per_blk, int K, int64_t n, int32_t *__restrict__ offsets,
     int32_t *__restrict__ perm, int32_t *__restrict__ inv) {
   __shared__ int32_t offs[MOE_ROUTE_MAX_EXPERTS + 1];
   __shared__ int32_t wave_tot[WAVES_PER_BLOCK];
@@ -518,7 +594,7 @@ __global__ __launch_bounds__(BLOCK) void scatter_kernel(
   const int rb0 = (int)((uint32_t)fb / kt);
   const int nrb = (int)((uint32_t)fe / kt) - rb0 + 1;
   const bool tabled = nrb * e_out <= SCATTER_TAB;  // block-uniform
-  const int stride = hist_stride(nblk);
+  const int stride = hist_stride(nblk, lg);
   // Every load of the first round (counts, the entries, the table) is issued
   // before any is used: clamped indices, no branches between them.
   int cx[4];
@@ -539,7 +615,7 @@ __global__ __launch_bounds__(BLOCK) void scatter_kernel(
   for (int h = 0; h < TAB_PER; ++h) {
     const int i = min((int)threadIdx.x + h * BLOCK, ntab - 1);
     const int rb = i / e_out;  // (route block rb0 + rb, id i - rb e_out)
-    tv[h] = hist[(size_t)(i - rb * e_out) * stride + hist_col(rb0 + rb, nblk)];
+    tv[h] = hist[(size_t)(i - rb * e_out) * stride + hist_col(rb0 + rb, nblk, lg)];
   }
   int cv[4];
 #pragma unroll
@@ -556,7 +632,7 @@ __global__ __launch_bounds__(BLOCK) void scatter_kernel(
 #pragma unroll
     for (int k = 0; k < SCATTER_PER_THREAD; ++k) {
       const int f = min(fb + (int)threadIdx.x + k * BLOCK, fe);
-      hv[k] = hist[(size_t)ev[k] * stride + hist_col((int)((uint32_t)f / kt), nblk)];
+      hv[k] = hist[(size_t)ev[k] * stride + hist_col((int)((uint32_t)f / kt), nblk, lg)];
     }
   }
   scan_store(cv, e_out, offs, wave_tot);  // its barriers also publish tab
@@ -825,15 +901,18 @@ static hipError_t launch_route(const float *logits, const float *bias, int T, co
   }
   if (qblocks > 0) mx_quant_kernel<<<qblocks, BLOCK, 0, st>>>(qa);
   const bool rows_path = LPG == 8 && NP == 7 && rows_path_applies(rp, logits);
-  const int tpb = rows_path ? ROWS_TOKENS_PER_BLOCK : WAVES_PER_BLOCK;
+  // count tiles: 16 tokens (row kernel, 2 per block) or 4 (one token per wave)
+  const int tpb = rows_path ? ROWS_TILE_TOKENS : WAVES_PER_BLOCK;
+  const int lg = rows_path ? ROWS_TILES_LG : 0;
   const int nblk = (T + tpb - 1) / tpb;
   PrefillCounts pc;
   pc.hist = reinterpret_cast<int32_t *>(ws + CONTROL_BYTES);
   pc.rank8 = reinterpret_cast<uint8_t *>(
-      ws + CONTROL_BYTES + align256((size_t)hist_stride(nblk) * rp.e_out * sizeof(int32_t)));
+      ws + CONTROL_BYTES + align256((size_t)hist_stride(nblk, lg) * rp.e_out * sizeof(int32_t)));
   // the benchmark hook's events are recorded by the launch itself
   if (rows_path) {
-    hipExtLaunchKernelGGL(route_rows_kernel, dim3(nblk), dim3(ROWS_BLOCK), 0, st, g_ev_before,
+    const int grid = (T + ROWS_TOKENS_PER_BLOCK - 1) / ROWS_TOKENS_PER_BLOCK;
+    hipExtLaunchKernelGGL(route_rows_kernel, dim3(grid), dim3(ROWS_BLOCK), 0, st, g_ev_before,
                           g_ev_after, 0, logits, bias, T, rp, o->topk_ids, o->topk_weights,
                           o->packed, pc);
   } else {
@@ -841,11 +920,12 @@ static hipError_t launch_route(const float *logits, const float *bias, int T, co
                           g_ev_before, g_ev_after, 0, logits, bias, T, rp, o->topk_ids,
                           o->topk_weights, o->packed, pc);
   }
-  block_prefix_kernel<<<rp.e_out, BLOCK, 0, st>>>(pc.hist, nblk, o->counts);
+  block_prefix_kernel<<<rp.e_out, BLOCK, 0, st>>>(pc.hist, nblk, lg, o->counts);
   const int64_t n = (int64_t)T * rp.K;
   const int64_t g3 = (n + BLOCK * SCATTER_PER_THREAD - 1) / (BLOCK * SCATTER_PER_THREAD);
   scatter_kernel<<<(int)g3, BLOCK, 0, st>>>(o->packed, pc.hist, pc.rank8, o->counts, rp.e_out,
-                                            nblk, tpb, rp.K, n, o->offsets, o->perm, o->inv_perm);
+                                            nblk, lg, tpb, rp.K, n, o->offsets, o->perm,
+                                            o->inv_perm);
   return hipGetLastError();
 }
 

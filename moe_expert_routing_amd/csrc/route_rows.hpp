@@ -64,6 +64,7 @@ constexpr int EG = 112;
 constexpr int LANES = 16;   // lanes per token (one DPP row)
 constexpr int NQP = 7;      // float4 loads per lane and pass
 constexpr int PP = 8;       // keys kept per lane and pass
+constexpr int PPS = PP;     // keys the streaming keeps
 constexpr int POOL = 10;    // merged keys of the kept groups per lane
 constexpr int MAX_K = 16;   // top_k handled by this path
 constexpr int MAX_CAND = 32;  // exact candidates per row in the refinement
@@ -80,19 +81,28 @@ template <> struct KeyWindow<1> {  // v in [2, 512)
   static constexpr uint32_t base = 0x40000000u;  // bits(2) = 16 * 2^26
   static constexpr float lo = 2.0f, hi = 503.0f;
 };
-constexpr int PREFETCH = 3;   // float4 loads in flight per lane
+constexpr int PREFETCH = 7;   // float4 loads in flight per lane (one pass)
+constexpr int NSTORE = 8;     // pool entries per pass the tournament reads from LDS
 
 constexpr int DPP_ROR4 = 0x124, DPP_ROR8 = 0x128, DPP_ROR12 = 0x12C;
 
-// Per-wave LDS of the row path, by row: winner / candidate ids, exact keys
-// and scores, the final (id, s) by slot.
+// Per-wave LDS of the row path. The tournament's pools (each lane's first
+// NSTORE keys of each pass, then a zero sentinel; [pass][i][lane], so the
+// lanes of a wave always read 64 different banks) are dead once the winners
+// are known, and share their space with the exact stage's candidate ids,
+// keys and final (id, s) by slot.
 struct RowScratch {
-  uint2 win[4][MAX_K];  // winner of extraction round k: (key, lane in the row)
-  int32_t cnt[4][LANES];
-  int32_t cand[4][MAX_CAND];
-  unsigned long long ekey[4][MAX_CAND];
-  uint2 slot[4][MAX_K];
-  float kth[4];
+  uint2 win[4][MAX_K];  // winner of tournament round k: (key, lane in the row)
+  union {
+    uint32_t pool[2][NSTORE + 1][64];
+    struct {
+      int32_t cnt[4][LANES];
+      int32_t cand[4][MAX_CAND];
+      unsigned long long ekey[4][MAX_CAND];
+      uint2 slot[4][MAX_K];
+      float kth[4];
+    };
+  };
 };
 
 // |v - (sp + B)| for a key value v, sp = RN32(RN32(sigma(x)) + b), sh = B > 0:
@@ -180,14 +190,13 @@ __device__ __forceinline__ void group_ranks(KT a, KT b, int &ra, int &rb) {
 }
 
 // Stages fl32(b + B) (in expert order) for a block of THREADS threads, for
-// both key windows (lds0: B = 1/2, lds1: B = 3). Returns the window every
-// bias fits (0 preferred), or -1 (block-uniform) when some bias fits neither
-// (or is not finite). `bad` holds one LDS word per wave. Every load is issued
+// the key window that every bias fits (0 preferred). Returns that window, or
+// -1 (block-uniform) when some bias fits neither (or is not finite); then
+// nothing is staged. `bad` holds one LDS word per wave. Every load is issued
 // before the first is used (clamped indices, no branches), so the staging
 // costs one memory round trip.
 template <int THREADS>
-__device__ __forceinline__ int stage_bias(const float *__restrict__ bias, float *lds0, float *lds1,
-                                          int *bad) {
+__device__ __forceinline__ int stage_bias(const float *__restrict__ bias, float *lds, int *bad) {
   constexpr int N = (E + THREADS - 1) / THREADS;
   float bb[N];
 #pragma unroll
@@ -198,14 +207,9 @@ __device__ __forceinline__ int stage_bias(const float *__restrict__ bias, float 
   bool ok0 = true, ok1 = true;
 #pragma unroll
   for (int k = 0; k < N; ++k) {
-    const int e = (int)threadIdx.x + k * THREADS;
-    if (e < E) {
-      const float v0 = bb[k] + KeyWindow<0>::shift, v1 = bb[k] + KeyWindow<1>::shift;
-      ok0 = ok0 && (v0 >= KeyWindow<0>::lo) && (v0 <= KeyWindow<0>::hi);
-      ok1 = ok1 && (v1 >= KeyWindow<1>::lo) && (v1 < KeyWindow<1>::hi);
-      lds0[e] = v0;
-      lds1[e] = v1;
-    }
+    const float v0 = bb[k] + KeyWindow<0>::shift, v1 = bb[k] + KeyWindow<1>::shift;
+    ok0 = ok0 && (v0 >= KeyWindow<0>::lo) && (v0 <= KeyWindow<0>::hi);
+    ok1 = ok1 && (v1 >= KeyWindow<1>::lo) && (v1 < KeyWindow<1>::hi);
   }
   const bool bad0 = __ballot(!ok0) != 0ull, bad1 = __ballot(!ok1) != 0ull;
   if ((threadIdx.x & 63) == 0) bad[threadIdx.x >> 6] = (bad0 ? 1 : 0) | (bad1 ? 2 : 0);
@@ -213,23 +217,43 @@ __device__ __forceinline__ int stage_bias(const float *__restrict__ bias, float 
   int any = 0;
 #pragma unroll
   for (int w = 0; w < THREADS / 64; ++w) any |= bad[w];
-  return (any & 1) == 0 ? 0 : ((any & 2) == 0 ? 1 : -1);
+  const int window = (any & 1) == 0 ? 0 : ((any & 2) == 0 ? 1 : -1);
+  if (window >= 0) {
+    const float sh = window == 0 ? KeyWindow<0>::shift : KeyWindow<1>::shift;
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      const int e = (int)threadIdx.x + k * THREADS;
+      if (e < E) lds[e] = bb[k] + sh;
+    }
+  }
+  __syncthreads();
+  return window;
+}
+
+// float4 n (n < 14) of a lane: pass n / 7, load n % 7 (float4 units from the
+// lane's first expert of the row).
+__host__ __device__ constexpr int lane_off(int n) { return (n / NQP) * EG + 4 * (n % NQP); }
+
+// Issues the lane's first PREFETCH float4 loads of the token at `row`.
+__device__ __forceinline__ void first_loads(const float *__restrict__ row, int c, int sub,
+                                            float4 (&xq)[PREFETCH]) {
+  const float4 *xp = reinterpret_cast<const float4 *>(row + c * EG + 4 * sub);
+#pragma unroll
+  for (int n = 0; n < PREFETCH; ++n) xq[n] = xp[lane_off(n)];
 }
 
 // Streams the lane's 56 experts of the token at `row`: keys into the sorted
-// top-8 of each pass (a: pass 0, b: pass 1).
+// top-8 of each pass (a: pass 0, b: pass 1). xq holds the first PREFETCH
+// loads (first_loads); the rest are issued here as those are consumed.
 __device__ __forceinline__ void stream_pools(const float *__restrict__ row,
                                              const float *__restrict__ bias_lds, int c, int sub,
-                                             uint32_t (&a)[PP], uint32_t (&b)[PP]) {
+                                             float4 (&xq)[PREFETCH], uint32_t (&a)[PP],
+                                             uint32_t (&b)[PP]) {
   const float4 *xp = reinterpret_cast<const float4 *>(row + c * EG + 4 * sub);
   const float4 *bp = reinterpret_cast<const float4 *>(bias_lds + c * EG + 4 * sub);
-  // float4 n (n < 14) of the lane: pass n / 7, load n % 7
-  auto off = [](int n) { return (n / NQP) * EG + 4 * (n % NQP); };
+  auto off = [](int n) { return lane_off(n); };
 #pragma unroll
   for (int i = 0; i < PP; ++i) a[i] = b[i] = 0u;
-  float4 xq[PREFETCH];
-#pragma unroll
-  for (int n = 0; n < PREFETCH; ++n) xq[n] = xp[off(n)];
 #pragma unroll
   for (int n = 0; n < 2 * NQP; ++n) {
     const float4 xv = xq[n % PREFETCH];
@@ -243,7 +267,7 @@ __device__ __forceinline__ void stream_pools(const float *__restrict__ row,
       const float v = fast_sigmoid(xs[j]) + bs[j];
       const uint32_t k = (__float_as_uint(v) << 6) | (uint32_t)(63 - (4 * n + j));
 #pragma unroll
-      for (int i = PP - 1; i > 0; --i) pl[i] = umed3(pl[i - 1], pl[i], k);
+      for (int i = PPS - 1; i > 0; --i) pl[i] = umed3(pl[i - 1], pl[i], k);
       pl[0] = umax(pl[0], k);
     }
     // materialise the pool here: otherwise the compiler sinks the lower
@@ -319,7 +343,7 @@ __device__ __forceinline__ void merge_kept(const uint32_t (&a)[PP], const uint32
 // last maximum (the (top_k+1)-th key). With win, the lane that wins round
 // rd < K writes (its key, u = its lane in the row) to win[rd].
 __device__ __forceinline__ uint32_t extract(const uint32_t (&m)[POOL], int K, uint32_t &rounds,
-                                            uint2 *win = nullptr, int u = 0) {
+                                            uint2 *win = nullptr, int u = 0, bool write = true) {
   uint32_t q[POOL];
 #pragma unroll
   for (int i = 0; i < POOL; ++i) q[i] = m[i];
@@ -328,11 +352,63 @@ __device__ __forceinline__ uint32_t extract(const uint32_t (&m)[POOL], int K, ui
   for (int rd = 0; rd <= K; ++rd) {
     M = row_max(q[0]);
     const bool won = q[0] == M;
-    if (win && won && rd < K) win[rd] = make_uint2(M, (uint32_t)u);
+    if (win && write && won && rd < K) win[rd] = make_uint2(M, (uint32_t)u);
     rounds = rounds + rounds + (won ? 1u : 0u);
 #pragma unroll
     for (int i = 0; i < POOL - 1; ++i) q[i] = won ? q[i + 1] : q[i];
   }
+  return M;
+}
+
+// LDS byte address of a shared-memory object, and a load from one.
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+__device__ __forceinline__ uint32_t lds_addr(uint32_t *p) {
+  return (uint32_t)(uintptr_t)(lds_u32 *)p;
+}
+__device__ __forceinline__ uint32_t lds_load(uint32_t addr) {
+  return *(const lds_u32 *)(uintptr_t)addr;
+}
+
+// top_k + 1 rounds of row maximum over the lanes' heads, each lane taking
+// the larger head of its two kept pass pools. The pools sit in LDS
+// (pool[pass][i][lane], first NSTORE keys, then zero), so a pop advances a
+// byte pointer instead of shifting registers; a dropped pass starts at the
+// zero sentinel. The lane that wins round rd < K writes (its key, u) to
+// win[rd]; ia / ib return the entries taken from each pass. Keys are never
+// zero (the slot field is at least 8), so a pointer stops at its sentinel.
+// Returns the last maximum (the (top_k+1)-th key).
+__device__ __forceinline__ uint32_t tournament(const uint32_t (&a)[PP], const uint32_t (&b)[PP],
+                                               bool kept_a, bool kept_b, int K,
+                                               uint32_t (*pool)[NSTORE + 1][64], int lane,
+                                               uint2 *win, int u, int &ia, int &ib) {
+#pragma unroll
+  for (int i = 0; i < NSTORE; ++i) {
+    pool[0][i][lane] = a[i];
+    pool[1][i][lane] = b[i];
+  }
+  pool[0][NSTORE][lane] = 0u;
+  pool[1][NSTORE][lane] = 0u;
+  // (each lane reads back only its own entries: LDS accesses of a wave stay
+  // in order)
+  constexpr uint32_t STRIDE = 64 * sizeof(uint32_t);
+  const uint32_t pa0 = lds_addr(&pool[0][kept_a ? 0 : NSTORE][lane]);
+  const uint32_t pb0 = lds_addr(&pool[1][kept_b ? 0 : NSTORE][lane]);
+  uint32_t pa = pa0, pb = pb0;
+  uint32_t ha = kept_a ? a[0] : 0u, hb = kept_b ? b[0] : 0u;
+  uint32_t M = 0u;
+  for (int rd = 0; rd <= K; ++rd) {
+    M = row_max(umax(ha, hb));
+    // (a zero head is a sentinel: it never advances, even in a degenerate row
+    // whose stored keys all tie and run out before K + 1 rounds)
+    const bool ta = ha == M && ha != 0u, tb = hb == M && hb != 0u;
+    if ((ta || tb) && rd < K) win[rd] = make_uint2(M, (uint32_t)u);
+    pa = ta ? pa + STRIDE : pa;
+    pb = tb ? pb + STRIDE : pb;
+    ha = lds_load(pa);
+    hb = lds_load(pb);
+  }
+  ia = (kept_a ? 0 : NSTORE) + (int)((pa - pa0) / STRIDE);
+  ib = (kept_b ? 0 : NSTORE) + (int)((pb - pb0) / STRIDE);
   return M;
 }
 
@@ -343,7 +419,7 @@ __device__ __forceinline__ uint32_t extract(const uint32_t (&m)[POOL], int K, ui
 __device__ __forceinline__ void row_outputs(bool out, uint2 sl, const RouteParams &p, int u,
                                             int64_t t, int32_t *__restrict__ ids,
                                             float *__restrict__ wts,
-                                            int32_t *__restrict__ packed) {
+                                            int32_t *__restrict__ packed, int32_t *lid) {
   const double sum = row_sum_f64(out ? (double)__uint_as_float(sl.y) : 0.0);
   if (out) {
     const int id = (int)sl.x;
@@ -354,7 +430,31 @@ __device__ __forceinline__ void row_outputs(bool out, uint2 sl, const RouteParam
     ids[o] = id;
     wts[o] = w;
     packed[o] = (int32_t)(((uint32_t)idp << 16) | bf16_rne_bits(w));
+    lid[u] = idp;
   }
+}
+
+// Row epilogue from binary64 scores: lane u of a row whose `out` is set
+// holds slot u's expert and score s, `sum` the row's sum of the K scores.
+__device__ __forceinline__ void row_store(bool out, int id, double s, double sum,
+                                          const RouteParams &p, int u, int64_t t,
+                                          int32_t *__restrict__ ids, float *__restrict__ wts,
+                                          int32_t *__restrict__ packed, int32_t *lid) {
+  if (out) {
+    const float w = (float)(s / sum);
+    int idp = id;
+    if (p.local) idp = (id >= p.off && id < p.off + p.cnt) ? id - p.off : p.cnt + u;
+    const size_t o = (size_t)t * p.K + u;
+    ids[o] = id;
+    wts[o] = w;
+    packed[o] = (int32_t)(((uint32_t)idp << 16) | bf16_rne_bits(w));
+    lid[u] = idp;
+  }
+}
+
+// Unit in the last place of a positive normal binary32 value.
+__device__ __forceinline__ float ulp32(float v) {
+  return __uint_as_float((__float_as_uint(v) & 0x7F800000u) - (23u << 23));
 }
 
 // Number of pool entries (sorted by key) whose value is >= thr.
@@ -445,6 +545,7 @@ __device__ __forceinline__ bool refine_rows(const float *__restrict__ row,
                                             bool need, bool groups_ok, bool kept_a_in,
                                             bool kept_b_in, uint32_t M_in, const RouteParams &p,
                                             int r, int u, int64_t t, RowScratch *L,
+                                            int32_t (*tids)[MAX_K],
                                             int32_t *__restrict__ ids, float *__restrict__ wts,
                                             int32_t *__restrict__ packed) {
   const int K = p.K;
@@ -470,7 +571,7 @@ __device__ __forceinline__ bool refine_rows(const float *__restrict__ row,
         (double)key_v<W>(p.topn == 2 ? b2 : b1) - 2.0 * (double)row_err(key_v<W>(b1), sh);
     const int na = regroup ? pool_count_ge<W>(a, thra) : 0;
     const int nb = regroup ? pool_count_ge<W>(b, thrb) : 0;
-    fail = row_max((na >= PP || nb >= PP) ? 1u : 0u) != 0u;
+    fail = row_max((na >= PPS || nb >= PPS) ? 1u : 0u) != 0u;
     uint32_t ta1, ta2, tb1, tb2;
     exact_top2_pair(row, bias_g, a, na, b, nb, c, sub, ta1, ta2, tb1, tb2);
     const float gxa = (p.topn == 2) ? ord_inv(ta1) + ord_inv(ta2) : ord_inv(ta1);
@@ -495,7 +596,7 @@ __device__ __forceinline__ bool refine_rows(const float *__restrict__ row,
   const double thb = (double)vm - 2.0 * (double)row_err(vm, sh);
   const int ca = (need && kept_a) ? pool_count_ge<W>(a, thb) : 0;
   const int cb = (need && kept_b) ? pool_count_ge<W>(b, thb) : 0;
-  fail = fail || row_max((ca >= PP || cb >= PP) ? 1u : 0u) != 0u;
+  fail = fail || row_max((ca >= PPS || cb >= PPS) ? 1u : 0u) != 0u;
   const int c2 = ca + cb;
   const int mc = (int)row_sum((uint32_t)c2);
   fail = fail || mc > MAX_CAND || mc < K;
@@ -554,7 +655,7 @@ __device__ __forceinline__ bool refine_rows(const float *__restrict__ row,
   const bool ok = ok_m && (double)L->kth[r] > bound;
   uint2 sl = make_uint2(0u, 0u);
   if (ok && u < K) sl = L->slot[r][u];
-  row_outputs(ok && u < K, sl, p, u, t, ids, wts, packed);
+  row_outputs(ok && u < K, sl, p, u, t, ids, wts, packed, tids[r]);
   return ok;
 }
 
@@ -563,89 +664,117 @@ __device__ __forceinline__ bool refine_rows(const float *__restrict__ row,
 // Returns a 4-bit mask of the rows that must be routed again by the
 // one-token-per-wave path; every other valid row has been written.
 template <int W>
-__device__ __forceinline__ uint32_t route_rows4(const float *__restrict__ logits,
-                                                const float *__restrict__ bias_g,
-                                                const float *__restrict__ bias_lds, int T,
-                                                int64_t t0, const RouteParams &p, int lane,
-                                                RowScratch *L, int32_t *__restrict__ ids,
-                                                float *__restrict__ wts,
-                                                int32_t *__restrict__ packed) {
+__device__ __forceinline__ uint32_t route_rows4_post(const uint32_t (&a)[PP],
+                                                     const uint32_t (&b)[PP],
+                                                     const float *__restrict__ logits,
+                                                     const float *__restrict__ bias_g,
+                                                     const float *__restrict__ bias_lds, int T,
+                                                     int64_t t0, const RouteParams &p, int lane,
+                                                     RowScratch *L, int32_t (*tids)[MAX_K],
+                                                     int32_t *__restrict__ ids,
+                                                     float *__restrict__ wts,
+                                                     int32_t *__restrict__ packed) {
   int ln = lane;
   asm volatile("" : "+v"(ln));
-  const int r = ln >> 4, u = ln & 15, c = u >> 2, sub = u & 3;
+  const int r = ln >> 4, u = ln & 15, c = u >> 2;
   const int64_t t = t0 + r;
   const bool valid = t < T;
   const float *row = logits + (size_t)(valid ? t : (int64_t)T - 1) * E;
   const int K = p.K;
-
-  // ---- streaming, groups, merged pool, extraction -----------------------------
-  // Issue priority by phase (s_setprio; measured about 1 us faster at 32K
-  // tokens): waves still streaming their rows go first, so every row's loads
-  // are in flight early; the selection runs at 1, the stores at 0; a wave
-  // that must refine a row goes first again, so that its extra work does not
-  // trail the rest of the grid.
-  uint32_t a[PP], b[PP];
-  __builtin_amdgcn_s_setprio(3);
-  stream_pools(row, bias_lds, c, sub, a, b);
+  // Issue priority by phase (s_setprio): waves still streaming their rows go
+  // first, so every row's loads are in flight early; the selection runs at
+  // 1, the stores at 0; a wave that must refine a row goes first again, so
+  // that its extra work does not trail the rest of the grid.
   __builtin_amdgcn_s_setprio(1);
   bool kept_a, kept_b;
   const bool groups_ok = approx_groups<W>(a, b, p, c, kept_a, kept_b);  // row-uniform
   bool fail = !groups_ok;
-  uint32_t m[POOL];
-  merge_kept(a, b, kept_a, kept_b, m);
-  uint32_t rounds;
-  const uint32_t M = extract(m, K, rounds, L->win[r], u);
-  const int pops = __popc(rounds);
-  const uint32_t total = row_sum((uint32_t)pops);
-  // exactly K+1 entries taken (no equal keys) and the merged pool not used up
-  fail = fail || total != (uint32_t)(K + 1) || pops >= POOL;
-  // a pass pool whose last key was taken (every key >= M was taken) may hide
-  // further keys of that group
-  fail = fail || (kept_a && a[PP - 1] >= M) || (kept_b && b[PP - 1] >= M);
+  int ia, ib;
+  const uint32_t M = tournament(a, b, kept_a, kept_b, K, L->pool, ln, L->win[r], u, ia, ib);
+  const int pops = (kept_a ? ia : 0) + (kept_b ? ib : 0);
+  // a pass whose pool was taken whole may hide further keys above M
+  fail = fail || (kept_a && ia == PP) || (kept_b && ib == PP);
+  // exactly K+1 entries taken (no equal keys)
+  fail = fail || row_sum((uint32_t)pops) != (uint32_t)(K + 1);
   wave_lds_sync();
 
-  // ---- exact scores of the winners; exact order by (sp desc, id asc) ---------------
+  // ---- slot order, boundary and weights from the approximate keys -------------------
+  // Lane u < K takes the winner of round u; rounds pop keys in descending
+  // order. |v - (sp + B)| <= row_err(v) for every key value v, so when
+  //  * every winner's value beats the next one's (the K-th winner's: M's) by
+  //    more than both errors, the exact (sp desc, id asc) order is the round
+  //    order and no other expert reaches the K-th exact score;
+  // the slots are certified. Weights: the key holds v = fl32(s~ + fl32(b+B)),
+  // so v - fl32(b+B) (exact in binary64) is within e = FAST_SIG_ERR_TESTED +
+  // ulp(v)/2 of the exact score s; w = s_k / sum s then moves by at most
+  // e_k/(s_k - e_k) + sum e/(sum s - sum e) relative, and two binary32
+  // roundings. A row is finished here when that stays within 0.9e-6 for every
+  // slot (inside the 1e-6 tolerance on weights); otherwise its winners are
+  // scored exactly below.
   const uint32_t pre_fail = row_max((fail && valid) ? 1u : 0u);
   const bool act = pre_fail == 0u && valid && u < K;
+  constexpr float sh = KeyWindow<W>::shift;
   int my_id = 0;
-  float my_s = 0.0f, my_sp = 0.0f;
+  double my_s = 0.0, my_e = 0.0;
+  bool ok = true;
   if (act) {
     const uint2 w = L->win[r][u];  // winner of round u: key and the lane holding it
-    my_id = key_expert(w.x, (int)(w.y >> 2), (int)(w.y & 3));
-    my_s = sigmoid_rn32(row[my_id]);
-    my_sp = my_s + bias_g[my_id];
-    L->ekey[r][u] = ((uint64_t)ord_f32(my_sp) << 32) | (uint64_t)(~(uint32_t)my_id);
+    // (every round of a row that took K + 1 keys had a winner, so w is this
+    // row's; the clamp only keeps the index inside the row)
+    my_id = min(key_expert(w.x, (int)(w.y >> 2) & 3, (int)(w.y & 3)), E - 1);
+    const float v = key_v<W>(w.x);
+    const float vn = u + 1 < K ? key_v<W>(L->win[r][u + 1].x) : key_v<W>(M);
+    ok = (double)v - (double)row_err(v, sh) > (double)vn + (double)row_err(vn, sh);
+    my_s = (double)v - (double)bias_lds[my_id];
+    my_e = (double)FAST_SIG_ERR_TESTED + 0.5 * (double)ulp32(v);
   }
-  // every expert outside the winners has a key below M: its exact score is at
-  // most key_v(M) - B + row_err(key_v(M)); the weakest winner must beat that
-  const float vm = key_v<W>(M);
-  const double bound = (double)vm - (double)KeyWindow<W>::shift + (double)row_err(vm, KeyWindow<W>::shift);
-  const uint32_t weakest = row_min(act ? ord_f32(my_sp) : 0xFFFFFFFFu);
-  const bool boundary_ok = (double)ord_inv(weakest) > bound;
-  wave_lds_sync();
-  int rank = 0;
-  if (act) {
-    const uint64_t mk = L->ekey[r][u];
-    for (int j = 0; j < K; ++j) rank += L->ekey[r][j] > mk ? 1 : 0;
-  }
-  const uint32_t row_fail = pre_fail | ((valid && !boundary_ok && pre_fail == 0u) ? 1u : 0u);
-
+  const double S = row_sum_f64(my_s), Se = row_sum_f64(my_e);
+  if (act)
+    ok = ok && my_s > 2.0 * my_e && S > 2.0 * Se &&
+         my_e / (my_s - my_e) + Se / (S - Se) + 0x1p-23 + 0x1p-40 <= 0.9e-6;
+  const bool approx_ok = pre_fail == 0u && row_min((act && !ok) ? 0u : 1u) != 0u;  // row-uniform
   __builtin_amdgcn_s_setprio(0);
-  // ---- epilogue: lane u takes slot u (the winner of exact rank u) ----------------
-  if (row_fail == 0u && act) L->slot[r][rank] = make_uint2((uint32_t)my_id, __float_as_uint(my_s));
-  wave_lds_sync();
-  const bool out = row_fail == 0u && act;
-  uint2 sl = make_uint2(0u, 0u);
-  if (out) sl = L->slot[r][u];
-  row_outputs(out, sl, p, u, t, ids, wts, packed);
+  row_store(approx_ok && act, my_id, my_s, S, p, u, t, ids, wts, packed, tids[r]);
+  bool done = approx_ok || !valid;
+
+  // ---- rows the keys cannot settle: exact scores of the same winners ----------------
+  const bool need_exact = valid && pre_fail == 0u && !approx_ok;  // row-uniform
+  if (__ballot(need_exact)) {
+    const bool ex = need_exact && u < K;
+    float es = 0.0f, esp = 0.0f;
+    if (ex) {
+      es = sigmoid_rn32(row[my_id]);
+      esp = es + bias_g[my_id];
+      L->ekey[r][u] = ((uint64_t)ord_f32(esp) << 32) | (uint64_t)(~(uint32_t)my_id);
+    }
+    // every expert outside the winners has a key below M: its exact score is
+    // at most key_v(M) - B + row_err(key_v(M)); the weakest winner must beat it
+    const float vm = key_v<W>(M);
+    const double bound = (double)vm - (double)sh + (double)row_err(vm, sh);
+    const uint32_t weakest = row_min(ex ? ord_f32(esp) : 0xFFFFFFFFu);
+    const bool boundary_ok = (double)ord_inv(weakest) > bound;
+    wave_lds_sync();
+    int rank = 0;
+    if (ex) {
+      const uint64_t mk = L->ekey[r][u];
+      for (int j = 0; j < K; ++j) rank += L->ekey[r][j] > mk ? 1 : 0;
+    }
+    const bool exact_ok = need_exact && boundary_ok;
+    if (exact_ok && ex) L->slot[r][rank] = make_uint2((uint32_t)my_id, __float_as_uint(es));
+    wave_lds_sync();
+    uint2 sl = make_uint2(0u, 0u);
+    if (exact_ok && u < K) sl = L->slot[r][u];
+    row_outputs(exact_ok && u < K, sl, p, u, t, ids, wts, packed, tids[r]);
+    done = done || exact_ok;
+  }
 
   // ---- rows whose certificate failed: exact refinement -------------------------
-  bool done = row_fail == 0u;
   const bool need = !done && valid;
   if (__ballot(need)) {
     __builtin_amdgcn_s_setprio(3);
     wave_lds_sync();
-    done = refine_rows<W>(row, bias_g, a, b, need, groups_ok, kept_a, kept_b, M, p, r, u, t, L, ids,
+    done = refine_rows<W>(row, bias_g, a, b, need, groups_ok, kept_a, kept_b, M, p, r, u, t, L, tids,
+                          ids,
                        wts, packed) ||
            done;
   }

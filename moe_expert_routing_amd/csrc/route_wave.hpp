@@ -186,6 +186,11 @@ __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > 
 // ---------------------------------------------------------------------------
 // Bound on |fast_sigmoid(x) - RN32(sigma(x))| over all finite binary32 x.
 constexpr float FAST_SIG_ERR = 0x1p-22f;
+// The bound the exhaustive GPU test of fast_sigmoid asserts over every finite
+// binary32 input: |fast_sigmoid(x) - RN32(sigma(x))| <= FAST_SIG_ERR / 2. It
+// bounds the unbiased scores the row path derives from its keys for the
+// weights (selection certificates keep the factor-two margin).
+constexpr float FAST_SIG_ERR_TESTED = 0.5f * FAST_SIG_ERR;
 
 __device__ __forceinline__ float fast_sigmoid(float x) {
   const float e = __builtin_amdgcn_exp2f(x * -1.44269504088896340736f);

@@ -189,13 +189,23 @@ def test_deterministic_across_calls():
 
 
 def test_decode_and_prefill_paths_agree():
+    """The single-launch decode path and the tiled prefill path select the
+    same experts in the same slots; their weights agree within the weight
+    tolerance (each is within 1e-6 of the oracle's; the prefill path may take
+    them from its certified approximate scores)."""
     c = W.long_prefill(T=256)
     say("case decode-vs-prefill")
     big = run_case(c)
     small_case = W.RouteCase("first64", c.logits[:64], c.bias, off=c.off, cnt=c.cnt)
     small = run_case(small_case)
-    for k in ("topk_ids", "topk_weights", "packed"):
-        assert np.array_equal(big[k][:64], small[k]), k
+    assert np.array_equal(big["topk_ids"][:64], small["topk_ids"])
+    assert np.array_equal(big["packed"][:64] >> 16, small["packed"] >> 16)
+    bf = np.abs((big["packed"][:64] & 0xFFFF).astype(np.int64) - (small["packed"] & 0xFFFF))
+    assert bf.max() <= 1
+    wb, ws = big["topk_weights"][:64].astype(np.float64), small["topk_weights"].astype(np.float64)
+    assert (np.abs(wb - ws) / ws).max() <= 2e-6
+    assert_parity(small, oracle_case(small_case), "decode path")
+    assert_parity(big, oracle_case(c), "prefill path")
 
 
 def test_global_and_local_entries_reach_the_gemm_in_the_same_order():
