@@ -134,6 +134,31 @@ int moe_route_local(const float *logits, const float *bias,
                     size_t workspace_bytes, void *stream);
 
 /*
+ * Allocation-free moe_route_local, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. Same arguments, checks and results as moe_route_local,
+ * without the workspace: the control block and the permutation's tile counts
+ * and ranks live in a static device array of MOE_ROUTE_NOALLOC_SCRATCH_BYTES,
+ * one copy per GPU, which the library holds until the process ends. Nothing
+ * is allocated, by the library or by any routine it calls. The first call on
+ * a device looks up that device's copy (the current device must be the
+ * stream's) and clears its control block on `stream`; every call leaves the
+ * control block zero again. All calls on one GPU share the array: calls that
+ * can overlap on one GPU (other streams, other threads) race and give wrong
+ * results; serialise them.
+ * A call whose scratch need exceeds the array returns MOE_ERR_WORKSPACE
+ * before any launch. The need is below moe_route_workspace_bytes(T, E', K);
+ * for 896 experts in 8 groups, top_k <= 16 and 16-byte aligned logits it is
+ * 256 + 4 E' * 16 ceil(T / 256) + T * top_k bytes (256-byte aligned parts),
+ * which admits up to 69,888 tokens with global ids (E' = 896).
+ */
+#define MOE_ROUTE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int moe_route_local_noalloc(const float *logits, const float *bias, int32_t num_tokens,
+                            const moe_route_params *params, int32_t local_expert_offset,
+                            int32_t num_local_experts, const moe_route_outputs *out,
+                            void *stream);
+
+/*
  * Workspace bytes needed by moe_router_gemm_route: the routing workspace
  * first (moe_route_workspace_bytes, same control-block rule), then the
  * router GEMM's split-K partial sums.

@@ -10,6 +10,7 @@ built library every call raises.
 Calls (same names as the C ABI):
     route(logits, bias, ...)                       -> moe_route
     route_local(logits, bias, off, cnt, ...)       -> moe_route_local
+    route_local_noalloc(logits, bias, off, cnt)    -> moe_route_local_noalloc
     router_gemm_route(hidden, weight, bias, ...)   -> moe_router_gemm_route
     local_num_experts(E, K, off, cnt)              -> moe_route_local_num_experts
     route_quant_local(logits, bias, hidden, ...)   -> moe_route_quant_local
@@ -55,6 +56,9 @@ EXPORTS = {
     "moe_route_local": (ctypes.c_int, [_c_vp, _c_vp, _c_i32, ctypes.POINTER(RouteParams),
                                        _c_i32, _c_i32, ctypes.POINTER(RouteOutputs), _c_vp,
                                        ctypes.c_size_t, _c_vp]),
+    "moe_route_local_noalloc": (ctypes.c_int, [_c_vp, _c_vp, _c_i32, ctypes.POINTER(RouteParams),
+                                               _c_i32, _c_i32, ctypes.POINTER(RouteOutputs),
+                                               _c_vp]),
     "moe_router_gemm_route_workspace_bytes": (ctypes.c_size_t,
                                               [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
     "moe_router_gemm_route": (ctypes.c_int, [_c_vp, _c_vp, _c_i32, _c_i32, _c_vp, _c_vp,
@@ -237,6 +241,35 @@ def route_local(logits: torch.Tensor, bias: torch.Tensor, local_expert_offset: i
                                ws.data_ptr(), ws.numel(), sh)
     if st:
         _check(st, "moe_route_local")
+    out["num_experts_out"] = e_out
+    return out
+
+
+def route_local_noalloc(logits: torch.Tensor, bias: torch.Tensor, local_expert_offset: int = 0,
+                        num_local_experts: int = 0, *, n_groups: int = 8, topk_group: int = 4,
+                        top_k: int = 16, group_topn: int = 2,
+                        out: Optional[Dict[str, torch.Tensor]] = None
+                        ) -> Dict[str, torch.Tensor]:
+    """moe_route_local_noalloc: route_local on the library's static scratch
+    (no workspace). With `out` given, the call allocates nothing."""
+    _require(logits, "logits", torch.float32, 2)
+    _require(bias, "bias", torch.float32, 1)
+    T, E = logits.shape
+    if bias.shape[0] != E:
+        raise MoeRouteError("bias must have num_experts elements")
+    e_loc = local_num_experts(E, top_k, local_expert_offset, num_local_experts)
+    e_out = e_loc if e_loc > 0 else E
+    dev = logits.device
+    if out is None:
+        out = alloc_outputs(T, top_k, e_out, dev)
+    prm = _params_ref(E, n_groups, topk_group, top_k, group_topn)
+    o = _outputs_struct(out)
+    with torch.cuda.device(dev):
+        st = lib().moe_route_local_noalloc(logits.data_ptr(), bias.data_ptr(), T, prm[1],
+                                           local_expert_offset, num_local_experts,
+                                           ctypes.byref(o), _stream_handle(dev))
+    if st:
+        _check(st, "moe_route_local_noalloc")
     out["num_experts_out"] = e_out
     return out
 

@@ -27,6 +27,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/moe_route.h"
 #include "internal.hpp"
 #include "route_rows.hpp"
@@ -854,25 +856,40 @@ static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 // Benchmark hook (moe_route_set_kernel_events).
 static hipEvent_t g_ev_before = nullptr, g_ev_after = nullptr;
 
-// Workspace: the control block, then for the prefill path the per-route-
-// block id counts hist[e'][nblk] and the entries' in-block ranks. Sized for
-// the route kernel with the fewest tokens per block (one token per wave).
-static size_t route_ws_bytes(int T, int e_out, int K) {
-  size_t b = CONTROL_BYTES;
-  if (T > MOE_ROUTE_MAX_FUSED_TOKENS) {
-    const size_t nblk = ((size_t)T + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK;
-    b += align256((size_t)hist_stride((int)nblk) * e_out * sizeof(int32_t));  // hist
-    b += align256((size_t)T * K);                    // rank8
-  }
-  return b;
-}
-
 // The four-tokens-per-wave path: 896 experts in 8 groups, top_k <= 16, and
 // kept lanes whose pools (6 usable keys each) can hold top_k + 1 entries;
 // float4 loads need 16-byte aligned rows.
 static bool rows_path_applies(const RouteParams &rp, const float *logits) {
   return rp.E == rows::E && rp.G == rows::G && rp.K <= rows::MAX_K &&
          12 * rp.TG >= rp.K + 1 && ((uintptr_t)logits % 16) == 0;
+}
+
+// Workspace layout of one call: the control block, then for the prefill path
+// the per-count-tile id counts hist[e'][tile] and the entries' in-tile ranks.
+// Count tiles hold 16 tokens on the four-tokens-per-wave path (two tiles per
+// route block), 4 on the one-token-per-wave path (one per block).
+struct WsLayout {
+  int tpb = 0, lg = 0, ntiles = 0;  // tokens per tile, log2 tiles per block, tiles
+  size_t hist = 0, rank8 = 0;       // byte offsets in the workspace
+  size_t bytes = CONTROL_BYTES;     // total
+};
+
+static WsLayout ws_layout(int T, int e_out, int K, bool rows_path) {
+  WsLayout w;
+  if (T <= MOE_ROUTE_MAX_FUSED_TOKENS) return w;
+  w.tpb = rows_path ? ROWS_TILE_TOKENS : WAVES_PER_BLOCK;
+  w.lg = rows_path ? ROWS_TILES_LG : 0;
+  w.ntiles = (T + w.tpb - 1) / w.tpb;
+  w.hist = CONTROL_BYTES;
+  w.rank8 = w.hist + align256((size_t)hist_stride(w.ntiles, w.lg) * e_out * sizeof(int32_t));
+  w.bytes = w.rank8 + align256((size_t)T * K);
+  return w;
+}
+
+// Bytes a caller's workspace must hold: the layout of the path with the
+// smallest count tiles (one token per wave), which bounds every path's.
+static size_t route_ws_bytes(int T, int e_out, int K) {
+  return ws_layout(T, e_out, K, false).bytes;
 }
 
 template <int NP, int LPG>
@@ -901,14 +918,11 @@ static hipError_t launch_route(const float *logits, const float *bias, int T, co
   }
   if (qblocks > 0) mx_quant_kernel<<<qblocks, BLOCK, 0, st>>>(qa);
   const bool rows_path = LPG == 8 && NP == 7 && rows_path_applies(rp, logits);
-  // count tiles: 16 tokens (row kernel, 2 per block) or 4 (one token per wave)
-  const int tpb = rows_path ? ROWS_TILE_TOKENS : WAVES_PER_BLOCK;
-  const int lg = rows_path ? ROWS_TILES_LG : 0;
-  const int nblk = (T + tpb - 1) / tpb;
+  const WsLayout wl = ws_layout(T, rp.e_out, rp.K, rows_path);
+  const int tpb = wl.tpb, lg = wl.lg, nblk = wl.ntiles;
   PrefillCounts pc;
-  pc.hist = reinterpret_cast<int32_t *>(ws + CONTROL_BYTES);
-  pc.rank8 = reinterpret_cast<uint8_t *>(
-      ws + CONTROL_BYTES + align256((size_t)hist_stride(nblk, lg) * rp.e_out * sizeof(int32_t)));
+  pc.hist = reinterpret_cast<int32_t *>(ws + wl.hist);
+  pc.rank8 = reinterpret_cast<uint8_t *>(ws + wl.rank8);
   // the benchmark hook's events are recorded by the launch itself
   if (rows_path) {
     const int grid = (T + ROWS_TOKENS_PER_BLOCK - 1) / ROWS_TOKENS_PER_BLOCK;
@@ -929,10 +943,10 @@ static hipError_t launch_route(const float *logits, const float *bias, int T, co
   return hipGetLastError();
 }
 
-int validate_route_call(const float *logits, const float *bias, int32_t T,
-                        const moe_route_params *prm, int32_t off, int32_t cnt,
-                        const moe_route_outputs *o, const void *workspace, size_t ws_bytes,
-                        int *e_out) {
+// Every check of a routing call except the workspace's.
+static int validate_route_args(const float *logits, const float *bias, int32_t T,
+                               const moe_route_params *prm, int32_t off, int32_t cnt,
+                               const moe_route_outputs *o, int *e_out) {
   int st = validate_params(prm);
   if (st != MOE_OK) return st;
   if (!o) return MOE_ERR_NULL;
@@ -944,24 +958,28 @@ int validate_route_call(const float *logits, const float *bias, int32_t T,
     return MOE_ERR_NULL;
   const int32_t e_local = moe_route_local_num_experts(prm->num_experts, prm->top_k, off, cnt);
   if (e_local < 0) return e_local;
-  const int eo = e_local > 0 ? e_local : prm->num_experts;
+  if ((uintptr_t)logits % 8 != 0 || (uintptr_t)bias % 8 != 0) return MOE_ERR_SHAPE;
+  *e_out = e_local > 0 ? e_local : prm->num_experts;
+  return MOE_OK;
+}
+
+int validate_route_call(const float *logits, const float *bias, int32_t T,
+                        const moe_route_params *prm, int32_t off, int32_t cnt,
+                        const moe_route_outputs *o, const void *workspace, size_t ws_bytes,
+                        int *e_out) {
+  int eo = 0;
+  const int st = validate_route_args(logits, bias, T, prm, off, cnt, o, &eo);
+  if (st != MOE_OK) return st;
   if (!workspace) return MOE_ERR_WORKSPACE;
   if (ws_bytes < route_ws_bytes(T, eo, prm->top_k)) return MOE_ERR_WORKSPACE;
   if ((uintptr_t)workspace % 8 != 0) return MOE_ERR_WORKSPACE;
-  if ((uintptr_t)logits % 8 != 0 || (uintptr_t)bias % 8 != 0) return MOE_ERR_SHAPE;
   if (e_out) *e_out = eo;
   return MOE_OK;
 }
 
 
-static int route_impl(const float *logits, const float *bias, int32_t T,
-                      const moe_route_params *prm, int32_t off, int32_t cnt,
-                      const moe_route_outputs *o, void *workspace, size_t ws_bytes,
-                      void *stream, const QuantArgs &qa = QuantArgs{nullptr, nullptr, nullptr, 0}) {
-  int e_out = 0;
-  const int st = validate_route_call(logits, bias, T, prm, off, cnt, o, workspace, ws_bytes,
-                                     &e_out);
-  if (st != MOE_OK) return st;
+static RouteParams route_params(const moe_route_params *prm, int32_t off, int32_t cnt,
+                                int e_out) {
   RouteParams rp;
   rp.E = prm->num_experts;
   rp.G = prm->n_groups;
@@ -975,9 +993,13 @@ static int route_impl(const float *logits, const float *bias, int32_t T,
   rp.cnt = cnt;
   rp.local = e_out != rp.E ? 1 : 0;
   rp.e_out = e_out;
+  return rp;
+}
 
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  char *ws = reinterpret_cast<char *>(workspace);
+// Launches a validated call on workspace `ws`.
+static int route_launch(const float *logits, const float *bias, int32_t T, const RouteParams &rp,
+                        const moe_route_outputs *o, char *ws, hipStream_t s,
+                        const QuantArgs &qa) {
   hipError_t err;
   // the 896-expert, 8-group shape gets constant lanes per group
   if (rp.E == 896 && rp.lpg == 8) {
@@ -996,6 +1018,77 @@ static int route_impl(const float *logits, const float *bias, int32_t T,
     default: return MOE_ERR_UNSUPPORTED;
   }
   return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+static int route_impl(const float *logits, const float *bias, int32_t T,
+                      const moe_route_params *prm, int32_t off, int32_t cnt,
+                      const moe_route_outputs *o, void *workspace, size_t ws_bytes,
+                      void *stream, const QuantArgs &qa = QuantArgs{nullptr, nullptr, nullptr, 0}) {
+  int e_out = 0;
+  const int st = validate_route_call(logits, bias, T, prm, off, cnt, o, workspace, ws_bytes,
+                                     &e_out);
+  if (st != MOE_OK) return st;
+  return route_launch(logits, bias, T, route_params(prm, off, cnt, e_out), o,
+                      reinterpret_cast<char *>(workspace), reinterpret_cast<hipStream_t>(stream),
+                      qa);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free routing (moe_route_local_noalloc): the workspace is a
+// static device array, one copy per GPU, held until the process ends. Host
+// code never passes the array's name to a kernel (on the host it is only a
+// stand-in for the symbol): its device address is looked up once per device
+// with that device current and kept in noalloc_ptr[device].
+// ---------------------------------------------------------------------------
+constexpr size_t NOALLOC_BYTES = MOE_ROUTE_NOALLOC_SCRATCH_BYTES;
+constexpr int NOALLOC_MAX_DEVICES = 64;
+static_assert(NOALLOC_BYTES % 256 == 0 && NOALLOC_BYTES >= CONTROL_BYTES, "scratch size");
+
+static __device__ __align__(256) uint8_t scratch[NOALLOC_BYTES];
+
+static std::mutex noalloc_mu;
+static char *noalloc_ptr[NOALLOC_MAX_DEVICES];
+
+__global__ void clear_words_kernel(uint32_t *__restrict__ p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
+}
+
+// The current device's scratch address; the first call on a device looks it
+// up and clears the control block on `st` (a fill kernel, so that a caller
+// may capture the call in a graph).
+static int noalloc_scratch(hipStream_t st, char **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(noalloc_mu);
+  if (noalloc_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return MOE_ERR_HIP;
+    clear_words_kernel<<<1, 64, 0, st>>>(reinterpret_cast<uint32_t *>(p),
+                                         (int)(CONTROL_BYTES / sizeof(uint32_t)));
+    if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
+    noalloc_ptr[dev] = reinterpret_cast<char *>(p);
+  }
+  *out = noalloc_ptr[dev];
+  return MOE_OK;
+}
+
+static int route_noalloc(const float *logits, const float *bias, int32_t T,
+                         const moe_route_params *prm, int32_t off, int32_t cnt,
+                         const moe_route_outputs *o, void *stream) {
+  int e_out = 0;
+  int st = validate_route_args(logits, bias, T, prm, off, cnt, o, &e_out);
+  if (st != MOE_OK) return st;
+  const RouteParams rp = route_params(prm, off, cnt, e_out);
+  if (ws_layout(T, e_out, rp.K, rows_path_applies(rp, logits)).bytes > NOALLOC_BYTES)
+    return MOE_ERR_WORKSPACE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char *ws = nullptr;
+  st = noalloc_scratch(s, &ws);
+  if (st != MOE_OK) return st;
+  return route_launch(logits, bias, T, rp, o, ws, s,
+                      QuantArgs{nullptr, nullptr, nullptr, 0});
 }
 
 }  // namespace moe
@@ -1045,6 +1138,14 @@ int moe_route_local(const float *logits, const float *bias, int32_t num_tokens,
                     size_t workspace_bytes, void *stream) {
   return moe::route_impl(logits, bias, num_tokens, params, local_expert_offset,
                          num_local_experts, out, workspace, workspace_bytes, stream);
+}
+
+int moe_route_local_noalloc(const float *logits, const float *bias, int32_t num_tokens,
+                            const moe_route_params *params, int32_t local_expert_offset,
+                            int32_t num_local_experts, const moe_route_outputs *out,
+                            void *stream) {
+  return moe::route_noalloc(logits, bias, num_tokens, params, local_expert_offset,
+                            num_local_experts, out, stream);
 }
 
 int moe_route_quant_local(const float *logits, const float *bias, int32_t num_tokens,

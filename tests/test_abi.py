@@ -121,6 +121,24 @@ def test_null_and_shape_validation(L):
     assert L.moe_route(FAKE, FAKE, 8, None, ctypes.byref(_outs()), FAKE, 1 << 20, None) == ERR_NULL
 
 
+def test_noalloc_validation(L):
+    prm = _params()
+    def call(T=8, off=0, cnt=0, p=prm, outs=None, logits=FAKE):
+        o = outs or _outs()
+        return L.moe_route_local_noalloc(logits, FAKE, T, ctypes.byref(p), off, cnt,
+                                         ctypes.byref(o), None)
+    assert call(T=-1) == ERR_SHAPE
+    assert call(logits=None) == ERR_NULL
+    assert call(outs=_outs(counts=None)) == ERR_NULL
+    assert call(off=890, cnt=10) == ERR_RANGE
+    assert call(p=_params(N=3)) == ERR_UNSUP
+    # the static scratch (16 MiB) holds 69,888 tokens at 896 global ids on the
+    # four-tokens-per-wave path; one more token is refused before any launch
+    assert call(T=69_889) == ERR_WS
+    assert call(T=69_889, logits=FAKE + 8) == ERR_WS      # one-token-per-wave tiles: larger
+    assert call(T=400_000, off=0, cnt=112) == ERR_WS       # E' = 128
+
+
 def test_router_gemm_validation(L):
     prm = _params()
     o = _outs()
