@@ -107,7 +107,11 @@ size_t moe_route_workspace_bytes(int32_t num_tokens, int32_t num_experts_out,
                                  int32_t top_k);
 
 /*
- * Route T tokens with global ids (E' = num_experts).
+ * Route T tokens with global ids (E' = num_experts): the routing of the
+ * fused route launch with no rank range, which keeps the global ids in the
+ * packed output ("[kimi-k3] Rank-local expert ids for the EP routed MoE
+ * (upstream #45544)", commit message, the Plumbing passage: the range
+ * arguments are optional and 0 keeps the global ids).
  *   logits   [T, E] fp32 router logits
  *   bias     [E]    fp32 correction bias (added for selection only)
  * Writes every buffer of `out`. T = 0 writes zero counts and offsets.
@@ -119,7 +123,11 @@ int moe_route(const float *logits, const float *bias, int32_t num_tokens,
               void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Route T tokens for one expert-parallel rank range. Identical to moe_route
+ * Route T tokens for one expert-parallel rank range ("[kimi-k3] Rank-local
+ * expert ids for the EP routed MoE (upstream #45544)", commit message: the
+ * pack epilogue's relabel, and the Plumbing passage, where the optional
+ * (local_expert_offset, num_local_experts) pair changes the packed output
+ * only and 0 keeps the global ids). Identical to moe_route
  * except for the packed ids and the permutation space: when the range
  * applies (moe_route_local_num_experts > 0), experts of the range are
  * written as id - local_expert_offset, and any other expert chosen in top-k

@@ -233,6 +233,83 @@ def test_global_and_local_entries_reach_the_gemm_in_the_same_order():
 
 
 # --------------------------------------------------------------------------
+# decode edges: negative bias offsets and scores that underflow to zero
+# --------------------------------------------------------------------------
+
+def _underflow_case(T, rank, offset, seed):
+    """N(0,1) logits with a bias moved by `offset`; every 4th row (from row
+    1) keeps 8 experts and pushes the others to logits <= -104, whose
+    sigmoid rounds to 0 so that their biased score is the bias alone (<= 0
+    here); every 4th row from row 3 keeps only one expert. The selection
+    then takes experts with s = 0 (weight 0)."""
+    rng = np.random.default_rng(seed)
+    logits = rng.standard_normal((T, 896), dtype=np.float32)
+    bias = (np.float32(0.01) * rng.standard_normal(896, dtype=np.float32) +
+            np.float32(offset)).astype(np.float32)
+    for t in range(T):
+        if t % 4 in (1, 3):
+            keep = rng.choice(896, size=8 if t % 4 == 1 else 1, replace=False)
+            row = (-104.0 - 16.0 * rng.random(896)).astype(np.float32)
+            row[keep] = logits[t, keep]
+            logits[t] = row
+    return W.RouteCase(f"underflow_T{T}_r{rank}_b{offset}", logits, bias,
+                       off=112 * rank, cnt=112)
+
+
+def _tied_underflow_case(T, rank, offset):
+    """Every expert's bias equal to `offset` and every logit <= -104 except
+    one expert per row: all other biased scores tie exactly at the bias, so
+    the top-k is decided by expert id alone; the kept expert takes weight 1."""
+    logits = np.full((T, 896), -110.0, np.float32)
+    logits[np.arange(T), (np.arange(T) * 131 + 7) % 896] = 0.25
+    return W.RouteCase(f"tied_underflow_T{T}_r{rank}_b{offset}", logits,
+                       np.full(896, offset, np.float32), off=112 * rank, cnt=112)
+
+
+@pytest.mark.parametrize("offset", [-0.3, -0.9, -3.0])
+@pytest.mark.parametrize("T", [1, 8, 16, 64])
+def test_decode_negative_bias_and_underflow(T, offset):
+    ranks = range(8) if T == 16 else (0, 3, 7)
+    for rank in ranks:
+        c = _underflow_case(T, rank, offset, seed=900 + 10 * T + rank)
+        say(f"case {c.name}")
+        got, want = run_case(c), oracle_case(c)
+        assert_parity(got, want, c.name)
+        M.exact_path_tokens(reset=True)
+        c2 = _tied_underflow_case(T, rank, offset)
+        say(f"case {c2.name}")
+        got2, want2 = run_case(c2), oracle_case(c2)
+        assert_parity(got2, want2, c2.name)
+        exact = M.exact_path_tokens(reset=True)
+        assert exact >= T, (c2.name, exact)  # exact ties: the exact pipeline decides
+        assert np.all(np.sort(got2["topk_weights"], axis=1)[:, -1] == 1.0)
+
+
+def test_wave_kernel_on_the_896_shape_with_8_byte_aligned_logits():
+    """Logits 8 but not 16 bytes aligned: the 896-expert, 8-group shape runs
+    the one-token-per-wave kernel (its float4 loads need 16-byte rows).
+    Near-tie rows show which kernel decided: the wave kernel rescores its
+    candidates, the four-tokens-per-wave kernel would refine its rows."""
+    c = _near_tie_case(T=1000, seed=13)
+    buf = torch.empty(1000 * 896 + 4, dtype=torch.float32, device=DEV)
+    base = (16 - buf.data_ptr() % 16) // 4 % 4       # first 16-byte aligned element
+    view = buf[base + 2: base + 2 + 1000 * 896].view(1000, 896)
+    assert view.data_ptr() % 16 == 8
+    view.copy_(torch.from_numpy(c.logits))
+    for path in (M.PATH_REFINED, M.PATH_RESCORED):
+        M.path_tokens(path, reset=True)
+    say("case T=1000 896/8 logits at an 8-byte offset")
+    out = M.route_local(view, to_dev(c.bias), c.off, c.cnt)
+    torch.cuda.synchronize()
+    got = {k: (v.cpu().numpy() if isinstance(v, torch.Tensor) else v) for k, v in out.items()}
+    assert_parity(got, oracle_case(c), "offset logits")
+    refined = M.path_tokens(M.PATH_REFINED, reset=True)
+    rescored = M.path_tokens(M.PATH_RESCORED, reset=True)
+    say(f"refined {refined}, rescored {rescored}")
+    assert refined == 0 and rescored > 0
+
+
+# --------------------------------------------------------------------------
 # the fast path's error bound and its fallback
 # --------------------------------------------------------------------------
 
