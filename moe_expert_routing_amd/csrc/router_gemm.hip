@@ -7,8 +7,8 @@
 // operands keep the hidden dimension contiguous, so each lane's MFMA operand
 // is one 16-byte run of 8 bf16 along K.
 //
-// Kernel. A block of 4 waves computes a TM (tokens) x TN (experts) tile on
-// the matrix cores; each wave owns a WM x WN sub-tile. K advances in stages
+// Kernel. A block of 4 or 8 waves computes a TM (tokens) x TN (experts)
+// tile on the matrix cores; each wave owns a WM x WN sub-tile. K advances in stages
 // of 64: each stage's A and B tiles go from global memory straight into LDS
 // (global_load_lds_dwordx4, no register staging), NS stage buffers deep, so
 // NS - 1 stages are in flight while one is consumed; the next stage's
@@ -18,9 +18,12 @@
 // (8 rows, one chunk) hit 8 different bank quads.
 //
 // Shapes (v_mfma_f32_16x16x32_bf16, 4 stage buffers). Decode (T <= 128),
-// bound by reading W once: 64 x 64 tiles, 32 x 32 per wave. Prefill:
-// 128 x 128 tiles, 64 x 64 per wave. (Measured on MI355X: 32x32x16 MFMA
-// tiles and deeper stage rings were both slower here.) When
+// bound by reading W once: 64 x 64 tiles, 4 waves of 32 x 32. Prefill:
+// 128 x 128 tiles, 8 waves of 32 x 64 (two per SIMD, so that one wave's
+// MFMAs run while the other waits on LDS or the barrier). (Measured on
+// MI355X: 32x32x16 MFMA tiles, 4 waves of 64 x 64, deeper or shallower
+// stage rings, and operands loaded straight into registers without LDS were
+// all slower here.) When
 // the tiles do not fill the chip, K is split into S equal ranges; each
 // writes its own fp32 partial and a second kernel sums the S partials in a
 // fixed order, so the result does not depend on timing. Blocks are numbered
@@ -46,26 +49,29 @@ constexpr int THREADS = 256;    // 4 waves
 constexpr int MAX_SPLITS = 16;
 constexpr int DECODE_MAX_T = 128;
 
-template <int TM_, int TN_, int WM_, int WN_, int MF_, int NS_>
+template <int TM_, int TN_, int WM_, int WN_, int MF_, int NS_, int NW_ = 4>
 struct Tile {
   static constexpr int TM = TM_, TN = TN_, WM = WM_, WN = WN_;
+  static constexpr int NW = NW_;    // waves per block
+  static constexpr int NTHREADS = 64 * NW;
   static constexpr int MF = MF_;    // MFMA tile: 16 (16x16x32) or 32 (32x32x16)
   static constexpr int NS = NS_;    // LDS stage buffers
   static constexpr int KMF = MF == 16 ? 32 : 16;  // K per MFMA
   static constexpr int KSTEPS = TK / KMF;
   static constexpr int WAVES_N = TN / WN;
-  static_assert((TM / WM) * (TN / WN) == 4, "four waves");
+  static_assert((TM / WM) * (TN / WN) == NW, "one wave tile per wave");
   static_assert(WM % MF == 0 && WN % MF == 0, "whole MFMA tiles");
   static constexpr int FM = WM / MF, FN = WN / MF;  // MFMA tiles per wave
   static constexpr int A_BYTES = TM * TK * 2, B_BYTES = TN * TK * 2;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   // one load instruction fills 8 LDS rows (64 lanes x 16 bytes)
-  static constexpr int A_LOADS = TM / 32, B_LOADS = TN / 32;  // per wave per stage
+  static constexpr int A_LOADS = TM / (8 * NW), B_LOADS = TN / (8 * NW);  // per wave per stage
+  static_assert(A_LOADS * 8 * NW == TM && B_LOADS * 8 * NW == TN, "whole loads");
   static constexpr int LOADS = A_LOADS + B_LOADS;
   static_assert((NS - 2) * LOADS <= 63, "vmcnt range");
 };
 using DecodeTile = Tile<64, 64, 32, 32, 16, 4>;
-using PrefillTile = Tile<128, 128, 64, 64, 16, 4>;
+using PrefillTile = Tile<128, 128, 32, 64, 16, 4, 8>;
 
 template <int MF>
 struct MfmaAcc;
@@ -122,7 +128,7 @@ __device__ __forceinline__ int tile_of_block(int b, int ntiles) {
 }
 
 template <class C>
-__global__ __launch_bounds__(THREADS, 1) void router_gemm_kernel(
+__global__ __launch_bounds__(C::NTHREADS, 1) void router_gemm_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, float *__restrict__ Cout,
     int T, int E, int H, int k_per_split, int m_tiles, int n_tiles) {
   typedef typename MfmaAcc<C::MF>::type Acc;
@@ -355,10 +361,10 @@ int moe_router_gemm_route(const uint16_t *hidden_bf16, const uint16_t *weight_bf
                        : logits_out;
     const int blocks = pl.m_tiles * pl.n_tiles * S;
     if (pl.decode)
-      router_gemm_kernel<DecodeTile><<<blocks, THREADS, 0, st>>>(
+      router_gemm_kernel<DecodeTile><<<blocks, DecodeTile::NTHREADS, 0, st>>>(
           hidden_bf16, weight_bf16, dst, T, E, H, H / S, pl.m_tiles, pl.n_tiles);
     else
-      router_gemm_kernel<PrefillTile><<<blocks, THREADS, 0, st>>>(
+      router_gemm_kernel<PrefillTile><<<blocks, PrefillTile::NTHREADS, 0, st>>>(
           hidden_bf16, weight_bf16, dst, T, E, H, H / S, pl.m_tiles, pl.n_tiles);
     if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
     if (S > 1) {
