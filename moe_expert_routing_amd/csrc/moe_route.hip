@@ -249,13 +249,16 @@ __global__ __launch_bounds__(BLOCK) void mx_quant_kernel(QuantArgs qa) {
 // Decode path: one launch for T <= 64, NW waves (one token each) per block.
 // With one routing block (T <= NW) the block builds the permutation right
 // after its own barrier, from its output ids kept in LDS. With several, every
-// block also writes its output ids into perm with device-scope (coherent)
-// stores, waits for them to complete and takes a ticket with a device-scope
-// atomic; the last block reads the ids back with device-scope loads and
-// builds the permutation over them. Nothing else it reads was written by
-// another block of the launch, so no device-wide fence (L2 write-back or
-// invalidate) is needed. Blocks past the routing blocks quantise the
-// activations.
+// block also writes its output ids into perm, and after a workgroup barrier
+// (its waves' stores happen before) thread 0 takes a ticket with a
+// device-scope acquire-release atomic; the block that takes the last ticket
+// reads every block's ids back from perm and builds the permutation over
+// them. The release half orders each block's id stores before its ticket,
+// the acquire half orders the last block's loads after every ticket before
+// its own, so the last block sees all ids (on gfx950 the compiler brackets
+// the atomic with an L2 write-back and an L2 invalidate). The last block
+// resets the ticket, so every call leaves it zero. Blocks past the routing
+// blocks quantise the activations.
 // ---------------------------------------------------------------------------
 constexpr int DECODE_ONE_BLOCK_WAVES = 8;  // T <= 8: one routing block
 
@@ -263,7 +266,8 @@ template <int NP, int LPG, int NW>
 __global__ __launch_bounds__(64 * NW) void route_decode_kernel(
     const float *__restrict__ logits, const float *__restrict__ bias, int T, RouteParams p,
     int32_t *__restrict__ ids, float *__restrict__ wts, int32_t *__restrict__ packed,
-    int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
+    int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+    int32_t *perm,  // (also the other blocks' ids: read and written across blocks)
     int32_t *__restrict__ inv, uint32_t *__restrict__ ticket, QuantArgs qa) {
   constexpr int THREADS = 64 * NW;
   // the one-block kernel is launched for T <= NW only
@@ -289,18 +293,18 @@ __global__ __launch_bounds__(64 * NW) void route_decode_kernel(
     load_lane_layout<NP, LPG>(bias, p, lane, b);
     const int idp =
         route_token<NP, LPG>(row, x, b, bias, p, lane, t, &scratch[wave], ids, wts, packed);
-    // the last block reads the output ids from a device-coherent copy, kept
-    // in perm until it writes the permutation there
-    if (MULTI && nroute > 1 && lane < p.K)
-      __hip_atomic_store(&perm[t * p.K + lane], idp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // the last block reads the output ids from perm, where they stay until
+    // it writes the permutation there
+    if (MULTI && nroute > 1 && lane < p.K) perm[t * p.K + lane] = idp;
     if (!MULTI && lane < p.K) own_ids[t * p.K + lane] = idp;  // the one block's ids, in LDS
   }
   if (MULTI && nroute > 1) {
-    // every coherent store of the block completed, then a ticket
-    __builtin_amdgcn_s_waitcnt(0);
+    // the block's id stores, then its ticket (release: those stores become
+    // visible to the device first; acquire: the last block's loads below see
+    // every other block's)
     __syncthreads();
     if (threadIdx.x == 0)
-      is_last = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+      is_last = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
                 (uint32_t)nroute - 1u;
     __syncthreads();
     if (!is_last) return;
@@ -323,8 +327,7 @@ __global__ __launch_bounds__(64 * NW) void route_decode_kernel(
     for (int h = 0; h < PER; ++h) {
       const int f = min((int)threadIdx.x + h * THREADS, n - 1);
       if constexpr (MULTI)
-        ev[h] = nroute > 1 ? __hip_atomic_load(&perm[f], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                           : packed[f] >> 16;
+        ev[h] = nroute > 1 ? perm[f] : packed[f] >> 16;
       else
         ev[h] = own_ids[f];
     }
