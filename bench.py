@@ -39,6 +39,7 @@ BYTES_PER_TOKEN_PATH = 3904     # logits 3584 + ids, weights, packed, perm, inv 
 BYTES_PER_TOKEN_ROUTE_KERNEL = 3776  # logits 3584 + ids, weights, packed (3 x 64)
 COPY_BYTES = 512 << 20
 PROFILE_PMC = os.path.join(ROOT, "profiles", "pmc_route_rows_long_prefill_32768.txt")
+PROFILE_BUSY = os.path.join(ROOT, "profiles", "pmc_valu_busy_lds_conflicts_bench_default.txt")
 # sources the routing kernels are built from (the router GEMM is not among them)
 ROUTE_SOURCES = ("internal.hpp", "moe_route.hip", "rn_sigmoid.hpp", "route_rows.hpp",
                  "route_wave.hpp")
@@ -56,7 +57,73 @@ def parse():
     ap.add_argument("--decode-calls", type=int, default=1000)
     ap.add_argument("--oracle-seconds", type=float, default=12.0)
     ap.add_argument("--skip-oracle", action="store_true")
+    ap.add_argument("--oracle-child", action="store_true", help=argparse.SUPPRESS)
     return ap.parse_args()
+
+
+ORACLE_THREAD_ENV = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")
+
+
+def oracle_child(seconds: float) -> None:
+    """The CPU oracle timed on the host (run as a child process with one BLAS
+    / OpenMP thread, before the parent touches the GPU): routed tokens/s on
+    the long-prefill workload (chunks of 1024 tokens, each a full oracle call
+    with the permutation, for up to `seconds`), and the best of three calls
+    on the tiny, decode-local and decode-sweep workloads."""
+    import numpy as np  # noqa: F401  (imported under the one-thread environment)
+
+    import oracle as O
+    import workloads as W
+
+    def call(c):
+        O.route_ref(c.logits, c.bias, n_groups=c.n_groups, topk_group=c.topk_group,
+                    top_k=c.top_k, group_topn=c.group_topn, local_expert_offset=c.off,
+                    num_local_experts=c.cnt)
+
+    def best_us(c, reps=3):
+        best = float("inf")
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            call(c)
+            best = min(best, time.perf_counter() - t0)
+        return round(best * 1e6, 1)
+
+    configs = {"tiny_global_8": best_us(W.tiny_global(8)),
+               "decode_local_16_rank3": best_us(W.decode_local(16))}
+    configs["decode_sweep_rank3"] = {f"T{T}": best_us(W.decode_sweep(T, 3))
+                                     for T in W.DECODE_SWEEP_T}
+    T = 32768
+    c0 = W.long_prefill(T)
+    chunk, done = 1024, 0
+    t_start = time.perf_counter()
+    while done < T and time.perf_counter() - t_start < seconds:
+        O.route_ref(c0.logits[done:done + chunk], c0.bias, local_expert_offset=c0.off,
+                    num_local_experts=c0.cnt)
+        done += chunk
+    el = time.perf_counter() - t_start
+    print(json.dumps({"tokens": done, "of": T, "chunk": chunk, "seconds": el,
+                      "configs_us_per_call_best_of_3": configs}), flush=True)
+
+
+def run_oracle_child(seconds: float):
+    """Starts oracle_child in a child process (one thread) and returns its
+    result, or None when it fails."""
+    import subprocess
+    env = dict(os.environ)
+    for k in ORACLE_THREAD_ENV:
+        env[k] = "1"
+    cmd = [sys.executable, os.path.abspath(__file__), "--oracle-child",
+           "--oracle-seconds", str(seconds)]
+    try:
+        res = subprocess.run(cmd, env=env, capture_output=True, text=True,
+                             timeout=seconds + 300)
+    except subprocess.TimeoutExpired:
+        log("bench: the oracle child timed out")
+        return None
+    if res.returncode != 0:
+        log(f"bench: the oracle child failed ({res.returncode}): {res.stderr[-500:]}")
+        return None
+    return json.loads(res.stdout.strip().splitlines()[-1])
 
 
 def cpu_model() -> str:
@@ -86,23 +153,41 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(digest: str):
-    """HBM bytes per launch of the route kernel from the committed rocprofv3
-    --pmc summary, if it was taken on the current kernel sources."""
-    if not os.path.exists(PROFILE_PMC):
-        return None
+def read_profile(path: str, digest: str) -> dict:
+    """key = value lines of a committed rocprofv3 summary, if it was taken on
+    the current kernel sources (else an empty dict)."""
+    if not os.path.exists(path):
+        return {}
     kv = {}
-    with open(PROFILE_PMC) as fh:
+    with open(path) as fh:
         for line in fh:
             if "=" in line and not line.startswith("#"):
                 k, v = line.split("=", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("source_digest") != digest:
-        return None
+    return kv if kv.get("source_digest") == digest else {}
+
+
+def read_traffic(digest: str):
+    """HBM bytes per launch of the route kernel from the committed rocprofv3
+    --pmc summary, if it was taken on the current kernel sources."""
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return float(read_profile(PROFILE_PMC, digest)["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def read_busy(digest: str) -> dict:
+    """VALU-busy and LDS bank-conflict percentages per kernel from the
+    committed rocprofv3 --pmc summary (VALUBusy, LDSBankConflict), if it was
+    taken on the current kernel sources."""
+    out = {}
+    for k, v in read_profile(PROFILE_BUSY, digest).items():
+        if k.endswith("_pct"):
+            try:
+                out[k] = float(v)
+            except ValueError:
+                pass
+    return out
 
 
 class HipEvents:
@@ -131,10 +216,21 @@ class HipEvents:
 
 def main():
     args = parse()
+    if args.oracle_child:
+        oracle_child(args.oracle_seconds)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(this library has no multi-GPU path).", file=sys.stderr)
         sys.exit(2)
+
+    # the CPU oracle first, in a child process, before anything here touches
+    # the GPU
+    oracle_res = None
+    if not args.skip_oracle:
+        log(f"bench: oracle on the host, one thread (up to {args.oracle_seconds:.0f} s of "
+            "long-prefill tokens, plus the small workloads)")
+        oracle_res = run_oracle_child(args.oracle_seconds)
 
     import numpy as np
     import torch
@@ -202,6 +298,7 @@ def main():
     kern_gbps = BYTES_PER_TOKEN_ROUTE_KERNEL * T / (kern_avg_ms * 1e-3) / 1e9
     digest = source_digest()
     traffic = read_traffic(digest)
+    busy = read_busy(digest)
     log(f"bench: {ms_per_step * 1e3:.1f} us/step, route kernel {kern_avg_ms * 1e3:.1f} us")
 
     # which kernel path the tokens of one step took
@@ -391,24 +488,18 @@ def main():
     # CPU oracle on a bounded sample of the same workload
     # ------------------------------------------------------------------
     cpu = None
-    if not args.skip_oracle:
-        import oracle as O
-        c0 = cases[0]
-        chunk = 1024
-        done = 0
-        log(f"bench: oracle on the host (about {args.oracle_seconds:.0f} s)")
-        t_start = time.perf_counter()
-        while done < T and time.perf_counter() - t_start < args.oracle_seconds:
-            O.route_ref(c0.logits[done:done + chunk], c0.bias,
-                        local_expert_offset=off, num_local_experts=cnt)
-            done += chunk
-        el = time.perf_counter() - t_start
+    if oracle_res is not None:
+        done, el = oracle_res["tokens"], oracle_res["seconds"]
         cpu = {"value": round(done / el, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
                "sample": f"first {done} of the {T} long-prefill tokens, routed in chunks of "
-                         f"{chunk} tokens (each chunk a full oracle call incl. permutation), "
-                         f"{el:.1f} s single-threaded Python+numpy on "
+                         f"{oracle_res['chunk']} tokens (each chunk a full oracle call incl. "
+                         f"permutation), {el:.1f} s of Python+numpy in a child process with "
+                         f"{', '.join(k + '=1' for k in ORACLE_THREAD_ENV)}, on "
                          f"{cpu_model() or platform.processor() or platform.machine()}, "
-                         f"{os.cpu_count()} host cores present"}
+                         f"{os.cpu_count()} host cores present",
+               "threads": 1,
+               "small_configs_us_per_call_best_of_3":
+                   oracle_res["configs_us_per_call_best_of_3"]}
 
     frac = kern_gbps / HBM_PEAK_GBPS
     res = {
@@ -447,7 +538,10 @@ def main():
                      "bytes_per_token": BYTES_PER_TOKEN_ROUTE_KERNEL,
                      "frac_of_copy": round(kern_gbps / copy_gbps, 4),
                      "traffic": (round(traffic, 0) if traffic is not None else None),
-                     "source_digest": digest},
+                     "source_digest": digest,
+                     "valu_busy_pct": busy.get("route_rows_valu_busy_pct"),
+                     "lds_bank_conflict_pct": busy.get("route_rows_lds_bank_conflict_pct")},
+        "counters_from_profiles": busy or None,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
