@@ -93,6 +93,7 @@ constexpr int DPP_ROR4 = 0x124, DPP_ROR8 = 0x128, DPP_ROR12 = 0x12C;
 // keys and final (id, s) by slot.
 struct RowScratch {
   uint2 win[4][MAX_K];  // winner of tournament round k: (key, lane in the row)
+  uint2 sink[64];       // the tournament's stores of lanes that did not win a round
   union {
     uint32_t pool[2][NSTORE + 1][64];
     struct {
@@ -362,6 +363,7 @@ __device__ __forceinline__ uint32_t extract(const uint32_t (&m)[POOL], int K, ui
 
 // LDS byte address of a shared-memory object, and a load from one.
 typedef __attribute__((address_space(3))) uint32_t lds_u32;
+typedef __attribute__((address_space(3))) uint64_t lds_u64;
 __device__ __forceinline__ uint32_t lds_addr(uint32_t *p) {
   return (uint32_t)(uintptr_t)(lds_u32 *)p;
 }
@@ -380,7 +382,8 @@ __device__ __forceinline__ uint32_t lds_load(uint32_t addr) {
 __device__ __forceinline__ uint32_t tournament(const uint32_t (&a)[PP], const uint32_t (&b)[PP],
                                                bool kept_a, bool kept_b, int K,
                                                uint32_t (*pool)[NSTORE + 1][64], int lane,
-                                               uint2 *win, int u, int &ia, int &ib) {
+                                               uint2 *win, uint2 *sink_row, int u, int &ia,
+                                               int &ib) {
 #pragma unroll
   for (int i = 0; i < NSTORE; ++i) {
     pool[0][i][lane] = a[i];
@@ -395,13 +398,18 @@ __device__ __forceinline__ uint32_t tournament(const uint32_t (&a)[PP], const ui
   const uint32_t pb0 = lds_addr(&pool[1][kept_b ? 0 : NSTORE][lane]);
   uint32_t pa = pa0, pb = pb0;
   uint32_t ha = kept_a ? a[0] : 0u, hb = kept_b ? b[0] : 0u;
+  const uint32_t win0 = (uint32_t)(uintptr_t)(lds_u64 *)win;
+  const uint32_t sink = (uint32_t)(uintptr_t)(lds_u64 *)&sink_row[lane];
   uint32_t M = 0u;
   for (int rd = 0; rd <= K; ++rd) {
     M = row_max(umax(ha, hb));
     // (a zero head is a sentinel: it never advances, even in a degenerate row
     // whose stored keys all tie and run out before K + 1 rounds)
     const bool ta = ha == M && ha != 0u, tb = hb == M && hb != 0u;
-    if ((ta || tb) && rd < K) win[rd] = make_uint2(M, (uint32_t)u);
+    // every lane stores (no branch): the round's winner to slot rd, the
+    // other lanes (and every lane in the last round) to their own sink word
+    *(lds_u64 *)(uintptr_t)(((ta || tb) && rd < K) ? win0 + 8u * (uint32_t)rd : sink) =
+        ((uint64_t)(uint32_t)u << 32) | M;
     pa = ta ? pa + STRIDE : pa;
     pb = tb ? pb + STRIDE : pb;
     ha = lds_load(pa);
@@ -690,7 +698,8 @@ __device__ __forceinline__ uint32_t route_rows4_post(const uint32_t (&a)[PP],
   const bool groups_ok = approx_groups<W>(a, b, p, c, kept_a, kept_b);  // row-uniform
   bool fail = !groups_ok;
   int ia, ib;
-  const uint32_t M = tournament(a, b, kept_a, kept_b, K, L->pool, ln, L->win[r], u, ia, ib);
+  const uint32_t M =
+      tournament(a, b, kept_a, kept_b, K, L->pool, ln, L->win[r], L->sink, u, ia, ib);
   const int pops = (kept_a ? ia : 0) + (kept_b ? ib : 0);
   // a pass whose pool was taken whole may hide further keys above M
   fail = fail || (kept_a && ia == PP) || (kept_b && ib == PP);
@@ -729,9 +738,14 @@ __device__ __forceinline__ uint32_t route_rows4_post(const uint32_t (&a)[PP],
     my_e = (double)FAST_SIG_ERR_TESTED + 0.5 * (double)ulp32(v);
   }
   const double S = row_sum_f64(my_s), Se = row_sum_f64(my_e);
-  if (act)
+  // e_k / (s_k - e_k) + Se / (S - Se) + 2^-23 + 2^-40 <= 0.9e-6, multiplied
+  // through by the two positive denominators (the 2^-40 term also covers the
+  // binary64 rounding of this check)
+  if (act) {
+    const double A = my_s - my_e, B = S - Se;
     ok = ok && my_s > 2.0 * my_e && S > 2.0 * Se &&
-         my_e / (my_s - my_e) + Se / (S - Se) + 0x1p-23 + 0x1p-40 <= 0.9e-6;
+         my_e * B + Se * A + (0x1p-23 + 0x1p-40) * (A * B) <= 0.9e-6 * (A * B);
+  }
   const bool approx_ok = pre_fail == 0u && row_min((act && !ok) ? 0u : 1u) != 0u;  // row-uniform
   __builtin_amdgcn_s_setprio(0);
   row_store(approx_ok && act, my_id, my_s, S, p, u, t, ids, wts, packed, tids[r]);
