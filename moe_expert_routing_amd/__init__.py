@@ -31,6 +31,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "_lib", "libmoe_route.so")
 
 MAX_FUSED_TOKENS = 64
+NOALLOC_SCRATCH_BYTES = 16 << 20  # MOE_ROUTE_NOALLOC_SCRATCH_BYTES
 
 _c_i32 = ctypes.c_int32
 _c_vp = ctypes.c_void_p
@@ -268,6 +269,10 @@ def route_local_noalloc(logits: torch.Tensor, bias: torch.Tensor, local_expert_o
         st = lib().moe_route_local_noalloc(logits.data_ptr(), bias.data_ptr(), T, prm[1],
                                            local_expert_offset, num_local_experts,
                                            ctypes.byref(o), _stream_handle(dev))
+    if st == -5:
+        raise MoeRouteError(
+            f"moe_route_local_noalloc failed: {T} tokens with {e_out} output ids need more "
+            f"scratch than the library's static {NOALLOC_SCRATCH_BYTES >> 20} MiB (-5)")
     if st:
         _check(st, "moe_route_local_noalloc")
     out["num_experts_out"] = e_out

@@ -219,3 +219,10 @@ def test_binding_fails_loudly_without_gpu_tensors():
     import torch
     with pytest.raises(M.MoeRouteError):
         M.route(torch.zeros(4, 896), torch.zeros(896))
+
+
+def test_binding_noalloc_limit_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define MOE_ROUTE_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m is not None
+    assert int(m.group(1)) << int(m.group(2)) == M.NOALLOC_SCRATCH_BYTES

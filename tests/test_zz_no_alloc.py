@@ -73,6 +73,6 @@ def test_largest_accepted_then_one_beyond_is_rejected():
     logits = torch.zeros((T, 896), dtype=torch.float32, device=DEV)
     bias = torch.zeros(896, dtype=torch.float32, device=DEV)
     say(f"case noalloc rejected T={T}")
-    with pytest.raises(M.MoeRouteError, match="workspace"):
+    with pytest.raises(M.MoeRouteError, match="static 16 MiB"):
         M.route_local_noalloc(logits, bias)
     _check(W.random_case(64, seed=40, off=0, cnt=0))   # later calls still work
