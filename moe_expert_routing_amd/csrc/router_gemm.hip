@@ -19,11 +19,14 @@
 //
 // Shapes (v_mfma_f32_16x16x32_bf16, 4 stage buffers). Decode (T <= 128),
 // bound by reading W once: 64 x 64 tiles, 4 waves of 32 x 32. Prefill:
-// 128 x 128 tiles, 8 waves of 32 x 64 (two per SIMD, so that one wave's
-// MFMAs run while the other waits on LDS or the barrier). (Measured on
-// MI355X: 32x32x16 MFMA tiles, 4 waves of 64 x 64, deeper or shallower
-// stage rings, and operands loaded straight into registers without LDS were
-// all slower here.) When
+// 128 x 128 tiles, 8 waves: each 64 x 64 wave tile is shared by two waves,
+// one taking the first K step of every stage and one the second, summed
+// through LDS at the end (two waves per SIMD, so that one wave's MFMAs run
+// while the other waits on LDS or the barrier, and the LDS fragment reads
+// per MFMA stay those of 64 x 64 tiles). (Measured on MI355X: 32x32x16 MFMA
+// tiles, 4 waves of 64 x 64, 8 waves of 32 x 64, deeper or shallower stage
+// rings, and operands loaded straight into registers without LDS were all
+// slower here.) When
 // the tiles do not fill the chip, K is split into S equal ranges; each
 // writes its own fp32 partial and a second kernel sums the S partials in a
 // fixed order, so the result does not depend on timing. Blocks are numbered
@@ -49,17 +52,21 @@ constexpr int THREADS = 256;    // 4 waves
 constexpr int MAX_SPLITS = 16;
 constexpr int DECODE_MAX_T = 128;
 
-template <int TM_, int TN_, int WM_, int WN_, int MF_, int NS_, int NW_ = 4>
+template <int TM_, int TN_, int WM_, int WN_, int MF_, int NS_, int NW_ = 4, int KS_ = 1>
 struct Tile {
   static constexpr int TM = TM_, TN = TN_, WM = WM_, WN = WN_;
   static constexpr int NW = NW_;    // waves per block
+  static constexpr int KS = KS_;    // waves sharing one wave tile, each on part of every stage's K
   static constexpr int NTHREADS = 64 * NW;
   static constexpr int MF = MF_;    // MFMA tile: 16 (16x16x32) or 32 (32x32x16)
   static constexpr int NS = NS_;    // LDS stage buffers
   static constexpr int KMF = MF == 16 ? 32 : 16;  // K per MFMA
   static constexpr int KSTEPS = TK / KMF;
+  static constexpr int KSW = KSTEPS / KS;  // MFMA K steps per wave and stage
+  static_assert(KSW * KS == KSTEPS, "whole K steps per wave");
   static constexpr int WAVES_N = TN / WN;
-  static_assert((TM / WM) * (TN / WN) == NW, "one wave tile per wave");
+  static constexpr int NWT = NW / KS;      // wave tiles per block
+  static_assert((TM / WM) * (TN / WN) * KS == NW, "every wave tile on KS waves");
   static_assert(WM % MF == 0 && WN % MF == 0, "whole MFMA tiles");
   static constexpr int FM = WM / MF, FN = WN / MF;  // MFMA tiles per wave
   static constexpr int A_BYTES = TM * TK * 2, B_BYTES = TN * TK * 2;
@@ -71,7 +78,7 @@ struct Tile {
   static_assert((NS - 2) * LOADS <= 63, "vmcnt range");
 };
 using DecodeTile = Tile<64, 64, 32, 32, 16, 4>;
-using PrefillTile = Tile<128, 128, 32, 64, 16, 4, 8>;
+using PrefillTile = Tile<128, 128, 64, 64, 16, 4, 8, 2>;
 
 template <int MF>
 struct MfmaAcc;
@@ -181,19 +188,21 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void router_gemm_kernel(
 #pragma unroll
       for (int v = 0; v < (int)(sizeof(Acc) / sizeof(float)); ++v) acc[i][j][v] = 0.f;
 
-  const int wm = (wave / C::WAVES_N) * C::WM, wn = (wave % C::WAVES_N) * C::WN;
+  // wave tile wt, its part kh of each stage's K steps
+  const int wt = wave % C::NWT, kh = wave / C::NWT;
+  const int wm = (wt / C::WAVES_N) * C::WM, wn = (wt % C::WAVES_N) * C::WN;
   // operand lane layout: row lane % MF of the MFMA tile, K run lane / MF
   const int fr = lane % MF, fq = lane / MF;
 
   // Fragments of one stage in registers, two sets: the next stage's
   // fragments are read from LDS while the current stage's MFMAs run.
-  bf16x8 fa[2][C::KSTEPS][C::FM], fb[2][C::KSTEPS][C::FN];
+  bf16x8 fa[2][C::KSW][C::FM], fb[2][C::KSW][C::FN];
   auto read_frags = [&](int s, int set) {
     const uint8_t *As = smem + (s % NS) * C::STAGE_BYTES;
     const uint8_t *Bs = As + C::A_BYTES;
 #pragma unroll
-    for (int ks = 0; ks < C::KSTEPS; ++ks) {
-      const int pos = ((ks * (C::KMF / 8) + fq) ^ (fr & 7)) * 16;
+    for (int ks = 0; ks < C::KSW; ++ks) {
+      const int pos = (((kh * C::KSW + ks) * (C::KMF / 8) + fq) ^ (fr & 7)) * 16;
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
         fa[set][ks][i] = *reinterpret_cast<const bf16x8 *>(As + (wm + MF * i + fr) * 128 + pos);
@@ -204,7 +213,7 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void router_gemm_kernel(
   };
   auto mfmas = [&](int set) {
 #pragma unroll
-    for (int ks = 0; ks < C::KSTEPS; ++ks)
+    for (int ks = 0; ks < C::KSW; ++ks)
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -237,6 +246,33 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void router_gemm_kernel(
     mfmas(1);
   }
   if (s < nk) mfmas(0);  // odd stage count: the last stage is in set 0
+
+  if constexpr (C::KS == 2) {
+    // The two waves of a wave tile summed in a fixed order (kh 0 + kh 1),
+    // through the stage buffers: same accumulator layout in both, so each
+    // lane adds the value at its own index.
+    static_assert(C::NWT * C::FM * C::FN * (int)sizeof(Acc) * 64 <= NS * C::STAGE_BYTES,
+                  "partials fit in the stage buffers");
+    constexpr int NV = (int)(sizeof(Acc) / sizeof(float));
+    float *red = reinterpret_cast<float *>(smem) + wt * (C::FM * C::FN * NV * 64);
+    __syncthreads();  // every wave is done with the stage buffers
+    if (kh == 1) {
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+          for (int v = 0; v < NV; ++v) red[((i * C::FN + j) * NV + v) * 64 + lane] = acc[i][j][v];
+    }
+    __syncthreads();
+    if (kh == 1) return;
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+        for (int v = 0; v < NV; ++v) acc[i][j][v] += red[((i * C::FN + j) * NV + v) * 64 + lane];
+  }
 
   // D of one MFMA tile: 16x16: row 4*(lane/16) + v, column lane % 16;
   // 32x32: row 8*(v/4) + 4*(lane/32) + v%4, column lane % 32.
