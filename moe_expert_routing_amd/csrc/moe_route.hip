@@ -286,6 +286,14 @@ __global__ __launch_bounds__(64 * NW) void route_decode_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int t = blockIdx.x * NW + wave;
+  // Thread i owns ids [IPT i, IPT i + IPT) in the permutation below. Their
+  // token masks are cleared now, in every routing block (LDS is per block;
+  // the block that builds the permutation is only known later), and the
+  // barrier after the routing orders the clearing before the first OR.
+  constexpr int IPT = MOE_ROUTE_MAX_EXPERTS / THREADS;
+  static_assert(IPT * THREADS == MOE_ROUTE_MAX_EXPERTS, "whole ids per thread");
+#pragma unroll
+  for (int j = 0; j < IPT; ++j) mask[IPT * threadIdx.x + j] = 0ull;
   if (t < T) {
     const float *row = logits + (size_t)t * p.E;
     float b[2 * NP], x[2 * NP];
@@ -334,25 +342,42 @@ __global__ __launch_bounds__(64 * NW) void route_decode_kernel(
   }
   // (every id is read into ev, and used, before the barriers below, so
   // before perm is written)
-  for (int i = threadIdx.x; i < p.e_out; i += THREADS) mask[i] = 0ull;
 #pragma unroll
   for (int h = 0; h < PER; ++h) {
     const int f = min((int)threadIdx.x + h * THREADS, max(n - 1, 0));
     tv[h] = p.K == 1 ? f : (int)__umulhi((uint32_t)f, kinv);
   }
-  __syncthreads();
 #pragma unroll
   for (int h = 0; h < PER; ++h)
     if ((int)threadIdx.x + h * THREADS < n) atomicOr(&mask[ev[h]], 1ull << tv[h]);
   __syncthreads();
-  for (int i = threadIdx.x; i < p.e_out; i += THREADS) {
-    const int c = __popcll(mask[i]);
-    offs[i] = c;
-    counts[i] = c;
+  // counts and exclusive offsets of the thread's ids: a wave scan of the
+  // threads' sums, then the earlier waves' totals
+  int c[IPT], sum = 0;
+#pragma unroll
+  for (int j = 0; j < IPT; ++j) {
+    const int e = IPT * (int)threadIdx.x + j;
+    c[j] = e < p.e_out ? __popcll(mask[e]) : 0;
+    sum += c[j];
   }
+  const int incl = wave_inclusive_scan(sum);
+  if (lane == 63) wave_tot[wave] = incl;
   __syncthreads();
-  block_exclusive_scan<THREADS>(offs, p.e_out, offs, wave_tot);  // in place: reads precede writes
-  for (int i = threadIdx.x; i <= p.e_out; i += THREADS) offsets[i] = offs[i];
+  int run = incl - sum;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) run += w < wave ? wave_tot[w] : 0;
+#pragma unroll
+  for (int j = 0; j < IPT; ++j) {
+    const int e = IPT * (int)threadIdx.x + j;
+    if (e < p.e_out) {
+      offs[e] = run;
+      counts[e] = c[j];
+      offsets[e] = run;
+    }
+    run += c[j];
+  }
+  if (threadIdx.x == 0) offsets[p.e_out] = n;
+  __syncthreads();
   // LDS reads for every slot (clamped entries are valid ids), stores for
   // the real entries
 #pragma unroll
