@@ -319,10 +319,18 @@ __device__ __forceinline__ void rank_candidates(WaveScratch *L, int lane, int m,
   const bool is_cand = lane < m;
   const uint64_t ck = ((uint64_t)ord_f32(sc) << 32) | (uint64_t)(~eid);
   if (is_cand) L->key[lane] = ck;
-  if (lane >= m && lane < ((m + 3) & ~3)) L->key[lane] = 0ull;  // pad to a multiple of 4
+  // pad to a multiple of 4, and up to 32 (zero keys rank below every candidate)
+  if (lane >= m && lane < max((m + 3) & ~3, 32)) L->key[lane] = 0ull;
   wave_lds_sync();
   int r = 0;
-  if (is_cand) {
+  if (m <= 32) {
+    // the usual case: all 32 keys read at once (one LDS round trip)
+    uint64_t kk[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) kk[j] = L->key[j];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) r += kk[j] > ck ? 1 : 0;
+  } else if (is_cand) {
     for (int j = 0; j < m; j += 4) {
       const uint64_t k0 = L->key[j], k1 = L->key[j + 1], k2 = L->key[j + 2], k3 = L->key[j + 3];
       r += (k0 > ck ? 1 : 0) + (k1 > ck ? 1 : 0) + (k2 > ck ? 1 : 0) + (k3 > ck ? 1 : 0);
