@@ -460,10 +460,6 @@ __device__ __forceinline__ void row_store(bool out, int id, double s, double sum
   }
 }
 
-// Unit in the last place of a positive normal binary32 value.
-__device__ __forceinline__ float ulp32(float v) {
-  return __uint_as_float((__float_as_uint(v) & 0x7F800000u) - (23u << 23));
-}
 
 // Number of pool entries (sorted by key) whose value is >= thr.
 template <int W>

@@ -192,6 +192,11 @@ constexpr float FAST_SIG_ERR = 0x1p-22f;
 // weights (selection certificates keep the factor-two margin).
 constexpr float FAST_SIG_ERR_TESTED = 0.5f * FAST_SIG_ERR;
 
+// Unit in the last place of a positive normal binary32 value.
+__device__ __forceinline__ float ulp32(float v) {
+  return __uint_as_float((__float_as_uint(v) & 0x7F800000u) - (23u << 23));
+}
+
 __device__ __forceinline__ float fast_sigmoid(float x) {
   const float e = __builtin_amdgcn_exp2f(x * -1.44269504088896340736f);
   return __builtin_amdgcn_rcpf(1.0f + e);
@@ -573,9 +578,42 @@ __device__ __forceinline__ bool select_token(const float *__restrict__ row,
     }
   }
   if (!EXACT && rescored && lane == 0) atomicAdd(&g_rescored_tokens, 1ull);
-  // the weights use the exact s of the winners
   const float wx = __uint_as_float(rr.y);
   my_id = (int)rr.x;
+  // Weights (w_k = s_k / sum s in binary64, rounded to binary32). From the
+  // fast scores when their error bound keeps every weight within 0.9e-6
+  // relative: |fast - RN32(sigma)| <= FAST_SIG_ERR_TESTED (tested on every
+  // binary32 input) and |RN32(sigma) - sigma| <= ulp(fast) (half an ulp of
+  // RN32(sigma), which is at most twice fast's), so with e_k their sum, w_k
+  // moves by at most e_k/(s_k - e_k) + sum e/(sum s - sum e) relative, and the
+  // final rounding adds 2^-23 (2^-40 covers the binary64 arithmetic here).
+  // Otherwise from the exact scores.
+  if (!EXACT) {
+    const bool in = lane < p.K;
+    const float sf = in ? fast_sigmoid(wx) : 0.0f;
+    const double s = sf;
+    const double e = in ? (double)FAST_SIG_ERR_TESTED + (double)ulp32(fmaxf(sf, 0x1p-126f)) : 0.0;
+    double S = s, Se = e;  // sums over lanes 0..K-1 (K <= 32), as in the epilogue
+    S += dpp_f64<DPP_XOR1>(S);
+    Se += dpp_f64<DPP_XOR1>(Se);
+    S += dpp_f64<DPP_XOR2>(S);
+    Se += dpp_f64<DPP_XOR2>(Se);
+    S += dpp_f64<DPP_HALF_MIRROR>(S);
+    Se += dpp_f64<DPP_HALF_MIRROR>(Se);
+    S += dpp_f64<DPP_MIRROR>(S);
+    Se += dpp_f64<DPP_MIRROR>(Se);
+    if (p.K > 16) {
+      S += __shfl_xor(S, 16);
+      Se += __shfl_xor(Se, 16);
+    }
+    const double A = s - e, B = S - Se;
+    const bool ok = !in || (s > 2.0 * e && S > 2.0 * Se &&
+                            e * B + Se * A + (0x1p-23 + 0x1p-40) * (A * B) <= 0.9e-6 * (A * B));
+    if (__ballot(!ok) == 0ull) {
+      my_s = sf;
+      return true;
+    }
+  }
   my_s = (lane < p.K) ? sigmoid_rn32(wx) : 0.0f;
   return true;
 }
