@@ -111,15 +111,6 @@ __device__ __forceinline__ void scan_store(const int (&v)[1024 / THREADS], int n
   lds_barrier();
 }
 
-// The same in one call (in may be LDS or global memory; in place allowed:
-// every read precedes every write).
-template <int THREADS = BLOCK>
-__device__ void block_exclusive_scan(const int32_t *in, int n, int32_t *out, int32_t *wave_tot) {
-  int v[1024 / THREADS];
-  scan_load<THREADS>(in, n, v);
-  scan_store<THREADS>(v, n, out, wave_tot);
-}
-
 // ---------------------------------------------------------------------------
 // Prefill permutation, part 1 (end of every prefill route block, all BLOCK
 // threads, after the block's outputs are written): per output id, the
