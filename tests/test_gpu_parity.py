@@ -89,6 +89,18 @@ def test_long_prefill_32k_full():
     assert load.max() / load.mean() > 7.0
 
 
+@pytest.mark.parametrize("off,cnt", [(0, 112), (0, 0)])
+def test_long_prefill_beyond_one_wave_round(off, cnt):
+    # 49,189 tokens: more route blocks than the row kernel keeps resident at
+    # once (1024 at 32,768 tokens), and a last block holding 5 tokens
+    T = 49189
+    base = W.long_prefill(T, variant=1)
+    c = W.RouteCase(f"long_prefill_T{T}_off{off}_cnt{cnt}", base.logits, base.bias, off=off,
+                    cnt=cnt)
+    say(f"case long_prefill T={T} off={off} cnt={cnt} (full oracle comparison)")
+    assert_parity(run_case(c), oracle_case(c), c.name)
+
+
 @pytest.mark.parametrize("T", [1, 64, 100, 129, 1000, 4096])
 def test_router_gemm_then_route(T):
     c = W.router_case(T)
