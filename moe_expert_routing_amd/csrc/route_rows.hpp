@@ -89,17 +89,15 @@ constexpr int DPP_ROR4 = 0x124, DPP_ROR8 = 0x128, DPP_ROR12 = 0x12C;
 // Per-wave LDS of the row path. The tournament's pools (each lane's first
 // NSTORE keys of each pass, then a zero sentinel; [pass][i][lane], so the
 // lanes of a wave always read 64 different banks) are dead once the winners
-// are known, and share their space with the exact stage's candidate ids,
-// keys and final (id, s) by slot.
+// are known, and share their space with the exact stage's candidate ids
+// and final (id, s) by slot.
 struct RowScratch {
   uint2 win[4][MAX_K];  // winner of tournament round k: (key, lane in the row)
   uint2 sink[64];       // the tournament's stores of lanes that did not win a round
   union {
     uint32_t pool[2][NSTORE + 1][64];
     struct {
-      int32_t cnt[4][LANES];
       int32_t cand[4][MAX_CAND];
-      unsigned long long ekey[4][MAX_CAND];
       uint2 slot[4][MAX_K];
       float kth[4];
     };
@@ -167,6 +165,36 @@ __device__ __forceinline__ double row_sum_f64(double v) {
 template <int CTRL>
 __device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
   return ((uint64_t)dpp<CTRL>((uint32_t)(v >> 32)) << 32) | dpp<CTRL>((uint32_t)v);
+}
+
+// Sum of v over the lanes before this one in its row: a Hillis-Steele scan by
+// row shifts (row_shr:n; a lane with no source n lanes down reads zero).
+__device__ __forceinline__ uint32_t row_exclusive_sum(uint32_t v) {
+  uint32_t s = v;
+  s += dpp<0x111>(s);
+  s += dpp<0x112>(s);
+  s += dpp<0x114>(s);
+  s += dpp<0x118>(s);
+  return s - v;
+}
+
+// Adds to rk_i the number of keys larger than k_i among ks[] of the other
+// lanes of the row (row_ror:D for D = 1..15; every lane's keys are unique or
+// zero, and zero never counts).
+template <int N, int D = 1>
+__device__ __forceinline__ void rank_in_row(const uint64_t (&ks)[N], int (&rk)[N]) {
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    const uint64_t o = dpp_u64<0x120 + D>(ks[j]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      rk[i] += o > ks[i] ? 1 : 0;
+      // a running count, not a sum tree over every rotation: the selection's
+      // register peak is here
+      asm volatile("" : "+v"(rk[i]));
+    }
+  }
+  if constexpr (D + 1 < LANES) rank_in_row<N, D + 1>(ks, rk);
 }
 
 // Ranks of the lane's two groups (keys a: group c, b: group c + 4) among
@@ -604,11 +632,7 @@ __device__ __forceinline__ bool refine_rows(const float *__restrict__ row,
   const int c2 = ca + cb;
   const int mc = (int)row_sum((uint32_t)c2);
   fail = fail || mc > MAX_CAND || mc < K;
-  L->cnt[r][u] = c2;
-  wave_lds_sync();
-  int excl = 0;
-#pragma unroll
-  for (int j = 0; j < LANES; ++j) excl += (j < u) ? L->cnt[r][j] : 0;
+  const int excl = (int)row_exclusive_sum((uint32_t)c2);
 #pragma unroll
   for (int i = 0; i < PP; ++i) {
     if (!__ballot(i < ca || i < cb)) break;
@@ -627,22 +651,12 @@ __device__ __forceinline__ bool refine_rows(const float *__restrict__ row,
                          : 0ull;
   const uint64_t k1 = v1 ? ((uint64_t)ord_f32(s1 + bias_g[e1]) << 32) | (uint64_t)(~(uint32_t)e1)
                          : 0ull;
-  if (v0) L->ekey[r][u] = k0;
-  if (v1) L->ekey[r][u + LANES] = k1;
-  wave_lds_sync();
-  // ranks by counting: keys of the row, four per step (zero past mc)
-  const int mmax = (int)wave_max_u32(ok_m ? (uint32_t)mc : 0u);
-  int rk0 = 0, rk1 = 0;
-  for (int j = 0; j < mmax; j += 4) {
-    uint64_t o[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) o[q] = (ok_m && j + q < mc) ? L->ekey[r][j + q] : 0ull;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      rk0 += o[q] > k0 ? 1 : 0;
-      rk1 += o[q] > k1 ? 1 : 0;
-    }
-  }
+  // ranks by counting the row's larger keys: the lane's other key, then
+  // every other lane's two (keys of absent candidates are zero)
+  const uint64_t ks[2] = {k0, k1};
+  int rk[2] = {k1 > k0 ? 1 : 0, k0 > k1 ? 1 : 0};
+  rank_in_row(ks, rk);
+  const int rk0 = rk[0], rk1 = rk[1];
   if (v0 && rk0 < K) {
     L->slot[r][rk0] = make_uint2((uint32_t)e0, __float_as_uint(s0));
     if (rk0 == K - 1) L->kth[r] = ord_inv((uint32_t)(k0 >> 32));
@@ -752,10 +766,11 @@ __device__ __forceinline__ uint32_t route_rows4_post(const uint32_t (&a)[PP],
   if (__ballot(need_exact)) {
     const bool ex = need_exact && u < K;
     float es = 0.0f, esp = 0.0f;
+    uint64_t ek[1] = {0ull};  // (exact score, lower id first); zero off the winners
     if (ex) {
       es = sigmoid_rn32(row[my_id]);
       esp = es + bias_g[my_id];
-      L->ekey[r][u] = ((uint64_t)ord_f32(esp) << 32) | (uint64_t)(~(uint32_t)my_id);
+      ek[0] = ((uint64_t)ord_f32(esp) << 32) | (uint64_t)(~(uint32_t)my_id);
     }
     // every expert outside the winners has a key below M: its exact score is
     // at most key_v(M) - B + row_err(key_v(M)); the weakest winner must beat it
@@ -763,12 +778,9 @@ __device__ __forceinline__ uint32_t route_rows4_post(const uint32_t (&a)[PP],
     const double bound = (double)vm - (double)sh + (double)row_err(vm, sh);
     const uint32_t weakest = row_min(ex ? ord_f32(esp) : 0xFFFFFFFFu);
     const bool boundary_ok = (double)ord_inv(weakest) > bound;
-    wave_lds_sync();
-    int rank = 0;
-    if (ex) {
-      const uint64_t mk = L->ekey[r][u];
-      for (int j = 0; j < K; ++j) rank += L->ekey[r][j] > mk ? 1 : 0;
-    }
+    int rk[1] = {0};
+    rank_in_row(ek, rk);
+    const int rank = rk[0];
     const bool exact_ok = need_exact && boundary_ok;
     if (exact_ok && ex) L->slot[r][rank] = make_uint2((uint32_t)my_id, __float_as_uint(es));
     wave_lds_sync();

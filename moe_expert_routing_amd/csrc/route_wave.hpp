@@ -95,8 +95,9 @@ constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2,3,0,1]
 constexpr int DPP_HALF_MIRROR = 0x141; // lane i <-> 7-i within 8
 constexpr int DPP_MIRROR = 0x140;      // lane i <-> 15-i within 16
 
-// Every DPP pattern used here reads an in-range lane, so no old value is
-// needed (bound_ctrl set, full masks).
+// No old value is needed (full masks, bound_ctrl set): the permutations read
+// an in-range lane, and a row shift (row_shr) reads zero where no lane lies
+// that far down in the row.
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
