@@ -36,13 +36,18 @@
 //     comparing unique integer group keys around the row (row_ror); the
 //     choice is certified by the margin between the kept and the dropped
 //     groups.
-//  3. The kept pools of a lane are merged (bitonic) into one sorted top-10;
-//     top_k + 1 rounds of row-maximum extraction over the heads give the
-//     winners, and the last bounds every other expert of the kept groups.
-//  4. The winners are scored exactly (RN32 sigmoid, fl32 bias add) and
-//     ranked by (sp desc, id asc); the result is accepted when the weakest
-//     winner's exact score beats that bound, exactly top_k + 1 keys were
-//     taken (no equal keys) and no pool was used up.
+//  3. Tournament: each lane writes its two pass pools to LDS; top_k + 1
+//     rounds of the row maximum over the heads of the lanes' kept pools, each
+//     advancing the winning lane's pointer, give the winners in order, and
+//     the last maximum M bounds every other expert of the kept groups. It
+//     must take exactly top_k + 1 keys (no equal keys) and use up no pool.
+//  4. Certificate from the keys: when each winner's value beats the next
+//     one's by more than both errors, the round order is the exact
+//     (sp desc, id asc) order and no other expert reaches the K-th score;
+//     when, in addition, the scores read off the keys keep every weight
+//     within 0.9e-6 of the exact one, the row is written from the keys.
+//     Otherwise the winners are scored exactly (RN32 sigmoid, fl32 bias add)
+//     and ranked, and that stands when the weakest one beats M's bound.
 // A row that fails a check is settled by an exact refinement in the same
 // layout (exact group scores, exact scores of every candidate in the error
 // band); only a row the refinement cannot decide either (ties denser than

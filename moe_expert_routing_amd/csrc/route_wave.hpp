@@ -27,6 +27,9 @@
 //     than the error (or are exact twins). Otherwise the candidates are
 //     scored EXACTLY and ranked by exact (sp, id), and the result is accepted
 //     when the exact top_k-th score beats that bound.
+//  5. Weights: from the winners' approximate scores when their tested error
+//     bound keeps every weight within 0.9e-6 of the exact one, otherwise from
+//     the winners' exact scores.
 // A token that fails a check runs the same pipeline on exact scores (only
 // the key truncation is left to bound), and if that cannot decide either
 // (near-ties within 16 ulp at the threshold), route_token_exact: exact
