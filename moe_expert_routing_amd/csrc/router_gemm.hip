@@ -211,6 +211,20 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void router_gemm_kernel(
         fb[set][ks][j] = *reinterpret_cast<const bf16x8 *>(Bs + (wn + MF * j + fr) * 128 + pos);
     }
   };
+  // Marks a register set's fragments as settled. stage_ready's wait (inside
+  // inline asm, which the compiler's wait insertion cannot see) has already
+  // drained their LDS reads; without this the compiler waits for every LDS
+  // read in flight before the set's first MFMA, including the next stage's
+  // fragment reads issued just before, so those could not overlap the MFMAs.
+  auto settle = [&](int set) {
+#pragma unroll
+    for (int ks = 0; ks < C::KSW; ++ks) {
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i) asm volatile("" : "+v"(fa[set][ks][i]));
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) asm volatile("" : "+v"(fb[set][ks][j]));
+    }
+  };
   auto mfmas = [&](int set) {
 #pragma unroll
     for (int ks = 0; ks < C::KSW; ++ks)
@@ -237,12 +251,12 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void router_gemm_kernel(
   int s = 0;
   for (; s + 1 < nk; s += 2) {
     stage_ready(s + 1);
+    settle(0);
     read_frags(s + 1, 1);
     mfmas(0);
-    if (s + 2 < nk) {
-      stage_ready(s + 2);
-      read_frags(s + 2, 0);
-    }
+    if (s + 2 < nk) stage_ready(s + 2);
+    settle(1);  // on both paths, so that the merge below carries no wait
+    if (s + 2 < nk) read_frags(s + 2, 0);
     mfmas(1);
   }
   if (s < nk) mfmas(0);  // odd stage count: the last stage is in set 0
