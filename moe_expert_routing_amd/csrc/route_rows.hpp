@@ -569,9 +569,10 @@ __device__ __forceinline__ void exact_top2_pair(const float *__restrict__ row,
 // Exact refinement of the rows with `need` set (call with the whole wave).
 // A row whose group choice the main path could not certify first gets exact
 // group scores, from every pool entry that can hold a group's top scores,
-// and a new extraction over the exactly kept groups; the other rows keep the
-// main path's kept groups and (top_k+1)-th key M. Then the exact top_k comes
-// from every kept-pool entry within twice the key error of M. Both steps
+// and, when the exactly kept groups differ from the main path's, a new
+// extraction over them; the other rows keep the main path's kept groups and
+// (top_k+1)-th key M. Then the exact top_k comes from every kept-pool entry
+// within twice the key error of M. Both steps
 // decide on exact scores, so they only fail when a pool is too short or the
 // candidates exceed MAX_CAND. Returns true (row-uniform) when the row has
 // been written.
@@ -617,14 +618,21 @@ __device__ __forceinline__ bool refine_rows(const float *__restrict__ row,
     group_ranks(((uint64_t)ord_f32(gxa) << 3) | (uint64_t)(7 - c),
                 ((uint64_t)ord_f32(gxb) << 3) | (uint64_t)(3 - c), ra, rb);
     // ---- extraction over the exactly kept groups ------------------------------
-    uint32_t m[POOL];
-    merge_kept(a, b, ra < p.TG, rb < p.TG, m);
-    uint32_t rounds;
-    const uint32_t Mx = extract(m, K, rounds);
+    // only for rows whose exactly kept groups differ from the tournament's:
+    // over the same groups its last maximum M already is the (top_k+1)-th key
+    const bool xa = ra < p.TG, xb = rb < p.TG;
+    const bool moved =
+        regroup && row_max((xa != kept_a_in || xb != kept_b_in) ? 1u : 0u) != 0u;  // row-uniform
+    if (__ballot(moved)) {
+      uint32_t m[POOL];
+      merge_kept(a, b, xa, xb, m);
+      uint32_t rounds;
+      const uint32_t Mx = extract(m, K, rounds);
+      if (moved) M = Mx;
+    }
     if (regroup) {
-      kept_a = ra < p.TG;
-      kept_b = rb < p.TG;
-      M = Mx;
+      kept_a = xa;
+      kept_b = xb;
     }
   }
 
