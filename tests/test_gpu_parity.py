@@ -120,6 +120,30 @@ def test_router_gemm_then_route(T):
     assert_parity(got, want, c.name)
 
 
+def test_router_gemm_decode_calls_in_a_row():
+    # Decode-sized GEMMs split K and sum the partials in a fixed order: calls
+    # of other sizes in between (other splits, other partial layouts in the
+    # same workspace) leave the control block zero, and a repeated call gives
+    # the same logits bit for bit.
+    first = {}
+    for T in (64, 8, 100, 1, 64, 8, 100):
+        c = W.router_case(T)
+        say(f"case router_gemm in a row T={T}")
+        out = M.router_gemm_route(to_dev(c.hidden.view(np.int16)), to_dev(c.weight.view(np.int16)),
+                                  to_dev(c.bias))
+        torch.cuda.synchronize()
+        assert_workspace_zero()
+        logits = out["logits"].cpu().numpy()
+        if T in first:
+            assert np.array_equal(logits, first[T]), f"T={T}: logits differ between calls"
+            continue
+        ref = O.router_logits_ref(c.hidden, c.weight)
+        bound = O.router_logits_bound(c.hidden, c.weight)
+        err = np.abs(logits.astype(np.float64) - ref)
+        assert np.all(err <= bound), f"T={T}: max err {err.max():.3g}"
+        first[T] = logits
+
+
 # --------------------------------------------------------------------------
 # edge cases
 # --------------------------------------------------------------------------
