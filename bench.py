@@ -481,8 +481,15 @@ def main():
         fn()
         us = time_calls(fn, 200 if Tg == 64 else 50)
         flops = 2.0 * Tg * W.E * W.H
+        # context: the same product through the vendor library (hipBLASLt via
+        # torch.mm, bf16 operands, fp32 output), GEMM only, no routing
+        hb, wb = hid.view(torch.bfloat16), wt.view(torch.bfloat16).t()
+        lib_fn = lambda hb=hb, wb=wb: torch.mm(hb, wb, out_dtype=torch.float32)
+        lib_fn()
+        lib_us = time_calls(lib_fn, 200 if Tg == 64 else 50)
         gemm[f"T{Tg}"] = {"us_per_call": round(us, 2),
-                          "tflops_incl_route": round(flops / (us * 1e-6) / 1e12, 2)}
+                          "tflops_incl_route": round(flops / (us * 1e-6) / 1e12, 2),
+                          "library_gemm_only_us_per_call": round(lib_us, 2)}
 
     # ------------------------------------------------------------------
     # CPU oracle on a bounded sample of the same workload
