@@ -88,10 +88,10 @@ def oracle_child(seconds: float) -> None:
             best = min(best, time.perf_counter() - t0)
         return round(best * 1e6, 1)
 
-    configs = {"tiny_global_8": best_us(W.tiny_global(8)),
-               "decode_local_16_rank3": best_us(W.decode_local(16))}
-    configs["decode_sweep_rank3"] = {f"T{T}": best_us(W.decode_sweep(T, 3))
-                                     for T in W.DECODE_SWEEP_T}
+    per_workload = {"tiny_global_8": best_us(W.tiny_global(8)),
+                    "decode_local_16_rank3": best_us(W.decode_local(16))}
+    per_workload["decode_sweep_rank3"] = {f"T{T}": best_us(W.decode_sweep(T, 3))
+                                          for T in W.DECODE_SWEEP_T}
     T = 32768
     c0 = W.long_prefill(T)
     chunk, done = 1024, 0
@@ -102,7 +102,7 @@ def oracle_child(seconds: float) -> None:
         done += chunk
     el = time.perf_counter() - t_start
     print(json.dumps({"tokens": done, "of": T, "chunk": chunk, "seconds": el,
-                      "configs_us_per_call_best_of_3": configs}), flush=True)
+                      "workloads_us_per_call_best_of_3": per_workload}), flush=True)
 
 
 def run_oracle_child(seconds: float):
@@ -509,8 +509,8 @@ def main():
                          f"{cpu_model() or platform.processor() or platform.machine()}, "
                          f"{os.cpu_count()} host cores present",
                "threads": 1,
-               "small_configs_us_per_call_best_of_3":
-                   oracle_res["configs_us_per_call_best_of_3"]}
+               "small_workloads_us_per_call_best_of_3":
+                   oracle_res["workloads_us_per_call_best_of_3"]}
 
     frac = kern_gbps / HBM_PEAK_GBPS
     res = {
