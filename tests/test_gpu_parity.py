@@ -189,6 +189,9 @@ def test_range_that_does_not_apply_keeps_global_ids():
     (896, 8, 8, 16, 2),     # every group kept
     (896, 8, 4, 16, 1),     # group score = group max
     (896, 8, 2, 8, 2),
+    (896, 8, 1, 16, 2),     # one group kept, top-16 (one token per wave: 12 TG < K + 1)
+    (896, 8, 1, 8, 2),      # one group kept on the row path: the top 9 from one quad's pools
+    (896, 8, 4, 1, 2),      # top-1: two tournament rounds, weight 1
     (256, 8, 4, 8, 2),
     (1024, 16, 4, 32, 2),
     (128, 64, 8, 4, 2),
