@@ -192,6 +192,8 @@ def test_range_that_does_not_apply_keeps_global_ids():
     (896, 8, 1, 16, 2),     # one group kept, top-16 (one token per wave: 12 TG < K + 1)
     (896, 8, 1, 8, 2),      # one group kept on the row path: the top 9 from one quad's pools
     (896, 8, 4, 1, 2),      # top-1: two tournament rounds, weight 1
+    (896, 8, 1, 11, 2),     # the largest top-k the row path takes with one kept group
+    (896, 8, 4, 32, 2),     # top-32: one token per wave; 160 entries in one decode block
     (256, 8, 4, 8, 2),
     (1024, 16, 4, 32, 2),
     (128, 64, 8, 4, 2),
