@@ -1,20 +1,23 @@
 // moe_route.hip - routing kernels for gfx950 and the C ABI of include/moe_route.h.
 //
 // Paths (all give identical results):
-//  * decode, T <= 64: ONE launch. Blocks of 4 waves route one token per wave
-//    and publish their outputs; the last block to arrive (ticket in the
-//    workspace control block) builds counts, offsets and the permutation from
-//    per-expert 64-bit token masks in LDS. With moe_route_quant_local, more
-//    blocks of the same launch quantise the activations to MXFP8.
+//  * decode, T <= 64: ONE launch, one token per wave. Up to 8 tokens one
+//    block of 8 waves routes them all and builds counts, offsets and the
+//    permutation after its own barrier; above, blocks of 4 waves publish
+//    their output ids and the last block to arrive (an acquire-release
+//    ticket in the workspace control block) builds them. Both use per-expert
+//    64-bit token masks in LDS. With moe_route_quant_local, more blocks of
+//    the same launch quantise the activations to MXFP8.
 //  * prefill, T > 64: three launches.
 //      route:   four tokens per wave (896 experts in 8 groups, route_rows.hpp)
 //               or one token per wave (other shapes); at the end of every
-//               block, per output id the block's entry count -> hist[e'][blk]
-//               and per entry its rank within the block -> rank8.
-//      prefix:  per output id, exclusive scan of hist[e'][:] over blocks;
+//               block, per count tile (16 or 4 tokens) and output id the
+//               tile's entry count -> hist[e'][tile], and per entry its rank
+//               among the tile's entries of that id -> rank8.
+//      prefix:  per output id, exclusive scan of hist[e'][:] over the tiles;
 //               total -> counts[e'].
 //      scatter: offsets = exclusive scan of counts; each entry goes to
-//               offsets[e'] + hist[e'][blk] + rank8[f].
+//               offsets[e'] + hist[e'][tile] + rank8[f].
 // Consumers of one call's counts and perm, one launch each: the grouped-GEMM
 // layout (moe_grouped_layout) and the static balancing plan over expert-
 // owning ranks (moe_balance_plan).
