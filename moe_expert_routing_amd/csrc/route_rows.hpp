@@ -135,7 +135,6 @@ __device__ __forceinline__ int key_expert(uint32_t k, int c, int sub) {
   const int qq = q - 28 * pass;
   return (c + 4 * pass) * EG + 4 * sub + 16 * (qq >> 2) + (qq & 3);
 }
-__device__ __forceinline__ bool key_pass1(uint32_t k) { return (int)(k & 63u) <= 63 - 28; }
 
 // Inverse of ord_f32.
 __device__ __forceinline__ float ord_inv(uint32_t o) {
@@ -372,22 +371,17 @@ __device__ __forceinline__ void merge_kept(const uint32_t (&a)[PP], const uint32
   m[9] = l[1];
 }
 
-// top_k + 1 rounds of row maximum over the heads of m (sorted, descending).
-// rounds: bit (K - round) set when this lane won that round; returns the
-// last maximum (the (top_k+1)-th key). With win, the lane that wins round
-// rd < K writes (its key, u = its lane in the row) to win[rd].
-__device__ __forceinline__ uint32_t extract(const uint32_t (&m)[POOL], int K, uint32_t &rounds,
-                                            uint2 *win = nullptr, int u = 0, bool write = true) {
+// top_k + 1 rounds of row maximum over the heads of m (sorted, descending),
+// each popping the winning lane's head; returns the last maximum (the
+// (top_k+1)-th key).
+__device__ __forceinline__ uint32_t extract(const uint32_t (&m)[POOL], int K) {
   uint32_t q[POOL];
 #pragma unroll
   for (int i = 0; i < POOL; ++i) q[i] = m[i];
   uint32_t M = 0u;
-  rounds = 0u;
   for (int rd = 0; rd <= K; ++rd) {
     M = row_max(q[0]);
     const bool won = q[0] == M;
-    if (win && write && won && rd < K) win[rd] = make_uint2(M, (uint32_t)u);
-    rounds = rounds + rounds + (won ? 1u : 0u);
 #pragma unroll
     for (int i = 0; i < POOL - 1; ++i) q[i] = won ? q[i + 1] : q[i];
   }
@@ -626,8 +620,7 @@ __device__ __forceinline__ bool refine_rows(const float *__restrict__ row,
     if (__ballot(moved)) {
       uint32_t m[POOL];
       merge_kept(a, b, xa, xb, m);
-      uint32_t rounds;
-      const uint32_t Mx = extract(m, K, rounds);
+      const uint32_t Mx = extract(m, K);
       if (moved) M = Mx;
     }
     if (regroup) {
