@@ -120,6 +120,31 @@ def test_router_gemm_then_route(T):
     assert_parity(got, want, c.name)
 
 
+@pytest.mark.parametrize("T,E,H,G,TG,K", [
+    (1, 256, 2048, 8, 4, 8),      # decode tiles, 4 expert tiles
+    (100, 256, 2048, 8, 4, 8),    # two token tiles of the decode shape
+    (300, 256, 2048, 8, 4, 8),    # prefill tiles, 2 expert tiles, split K
+    (64, 1024, 1024, 16, 4, 16),  # 16 expert tiles
+    (129, 1024, 1024, 16, 4, 16),
+    (2000, 128, 512, 8, 4, 4),    # one expert tile, 16 token tiles
+])
+def test_router_gemm_other_shapes(T, E, H, G, TG, K):
+    c = W.router_case(T, e=E, h=H)
+    say(f"case router_gemm T={T} E={E} H={H}")
+    out = M.router_gemm_route(to_dev(c.hidden.view(np.int16)), to_dev(c.weight.view(np.int16)),
+                              to_dev(c.bias), n_groups=G, topk_group=TG, top_k=K)
+    torch.cuda.synchronize()
+    assert_workspace_zero()
+    logits = out["logits"].cpu().numpy()
+    ref = O.router_logits_ref(c.hidden, c.weight)
+    bound = O.router_logits_bound(c.hidden, c.weight)
+    err = np.abs(logits.astype(np.float64) - ref)
+    assert np.all(err <= bound), f"max err {err.max():.3g}"
+    got = {k: (v.cpu().numpy() if isinstance(v, torch.Tensor) else v) for k, v in out.items()}
+    want = O.route_ref(logits, c.bias, n_groups=G, topk_group=TG, top_k=K)
+    assert_parity(got, want, c.name)
+
+
 def test_router_gemm_decode_calls_in_a_row():
     # Decode-sized GEMMs split K and sum the partials in a fixed order: calls
     # of other sizes in between (other splits, other partial layouts in the

@@ -142,13 +142,16 @@ def decode_sweep(T: int, rank: int) -> RouteCase:
                      off=RANGE * rank, cnt=RANGE, meta={"rank": rank})
 
 
-def router_case(T: int) -> RouteCase:
-    """bf16 hidden [T, 7168] ~ N(0,1) and bf16 router weight [896, 7168] ~ N(0, 0.02)."""
-    rng = np.random.default_rng(seed_for(3, T))
-    hidden = _to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
-    weight = _to_bf16_bits(np.float32(0.02) * rng.standard_normal((E, H), dtype=np.float32))
-    bias = normal_bias(rng)
-    return RouteCase(f"router_T{T}", None, bias, hidden=hidden, weight=weight)
+def router_case(T: int, e: int = E, h: int = H) -> RouteCase:
+    """bf16 hidden [T, h] ~ N(0,1) and bf16 router weight [e, h] ~ N(0, 0.02)
+    (by default the 896 x 7168 router)."""
+    variant = 0 if (e, h) == (E, H) else 1 + e + h
+    rng = np.random.default_rng(seed_for(3, T, variant))
+    hidden = _to_bf16_bits(rng.standard_normal((T, h), dtype=np.float32))
+    weight = _to_bf16_bits(np.float32(0.02) * rng.standard_normal((e, h), dtype=np.float32))
+    bias = normal_bias(rng, e)
+    name = f"router_T{T}" if variant == 0 else f"router_T{T}_E{e}_H{h}"
+    return RouteCase(name, None, bias, hidden=hidden, weight=weight)
 
 
 def zipf_bias(rng: np.random.Generator, e: int = E, alpha: float = ZIPF_ALPHA,
