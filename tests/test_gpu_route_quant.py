@@ -57,6 +57,9 @@ CASES = [
     ("one_token", lambda: W.random_case(1, seed=3, off=0, cnt=112), 512),
     ("ragged100", lambda: W.random_case(100, seed=4, off=448, cnt=112), 512),
     ("t1000", lambda: W.random_case(1000, seed=5), 1024),
+    ("h32", lambda: W.random_case(5, seed=6, off=112, cnt=112), 32),      # one scale block per row
+    ("h96", lambda: W.random_case(64, seed=7), 96),                       # three blocks, 12 chunks
+    ("t65", lambda: W.random_case(65, seed=8, off=784, cnt=112), 7168),   # first size past one launch
 ]
 
 
