@@ -26,9 +26,14 @@ CASES = {
 
 
 @functools.lru_cache(maxsize=None)
-def _case(name):
+@functools.lru_cache(maxsize=None)
+def _case_and_oracle(name):
     c = CASES[name]()
-    want = O.route_ref(c.logits, c.bias)            # global ids
+    return c, O.route_ref(c.logits, c.bias)          # global ids
+
+
+def _case(name):
+    c, want = _case_and_oracle(name)
     out = M.route(to_dev(c.logits), to_dev(c.bias))
     torch.cuda.synchronize()
     got_counts = out["counts"].cpu().numpy()
@@ -37,7 +42,7 @@ def _case(name):
 
 
 @pytest.mark.parametrize("name", list(CASES))
-@pytest.mark.parametrize("n_ranks", [2, 7, 8, 16])
+@pytest.mark.parametrize("n_ranks", [1, 2, 7, 8, 16, 32, 64])
 def test_balance_plan_matches_oracle(name, n_ranks):
     c, want, out = _case(name)
     n = int(want["perm"].shape[0])

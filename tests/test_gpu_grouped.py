@@ -41,7 +41,7 @@ def _route(c):
 
 
 @pytest.mark.parametrize("name", list(CASES))
-@pytest.mark.parametrize("tile", [1, 64, 128])
+@pytest.mark.parametrize("tile", [1, 3, 64, 128, 4096])
 def test_grouped_layout_matches_oracle(name, tile):
     c, want = _case_and_oracle(name)
     say(f"case grouped layout {name} tile={tile}")
