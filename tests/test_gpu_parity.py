@@ -7,7 +7,8 @@ import torch
 import moe_expert_routing_amd as M
 import oracle as O
 import workloads as W
-from gpu_util import DEV, assert_parity, assert_workspace_zero, oracle_case, run_case, say, to_dev
+from gpu_util import (DEV, assert_parity, assert_workspace_zero, oracle_case, run_case, say,
+                      to_dev, to_numpy)
 
 pytestmark = [
     pytest.mark.gpu,
@@ -243,6 +244,31 @@ def test_extreme_logits_and_dense_ties():
     assert_parity(run_case(c), oracle_case(c), c.name)
     c2 = W.RouteCase("extreme_bias", logits, (0.01 * rng.standard_normal(896)).astype(np.float32))
     assert_parity(run_case(c2), oracle_case(c2), c2.name)
+
+
+def test_two_streams_route_concurrently():
+    # Calls on two streams of one device, not synchronised with each other:
+    # each stream has its own default workspace (the 16-token decode's
+    # ticket, the 4099-token prefill's tile counts), so every call returns
+    # exactly what the same call returns alone.
+    ca = W.decode_local(16)
+    cb = W.random_case(4099, seed=77, off=448, cnt=112)
+    say("case two streams: decode T=16 and prefill T=4099")
+    alone_a, alone_b = run_case(ca), run_case(cb)
+    la, ba, lb, bb = to_dev(ca.logits), to_dev(ca.bias), to_dev(cb.logits), to_dev(cb.bias)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()  # default priority
+    torch.cuda.synchronize()
+    outs = []
+    for _ in range(8):
+        with torch.cuda.stream(sa):
+            outs.append(("a", M.route_local(la, ba, ca.off, ca.cnt)))
+        with torch.cuda.stream(sb):
+            outs.append(("b", M.route_local(lb, bb, cb.off, cb.cnt)))
+    torch.cuda.synchronize()
+    for which, out in outs:
+        got, want = to_numpy(out), (alone_a if which == "a" else alone_b)
+        for k in ("topk_ids", "topk_weights", "packed", "counts", "offsets", "perm", "inv_perm"):
+            assert np.array_equal(got[k], want[k]), f"stream {which}: {k} differs"
 
 
 def test_deterministic_across_calls():
