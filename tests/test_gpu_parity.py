@@ -271,6 +271,43 @@ def test_two_streams_route_concurrently():
             assert np.array_equal(got[k], want[k]), f"stream {which}: {k} differs"
 
 
+@pytest.mark.parametrize("T", [8, 16, 4099])
+def test_graph_replays_match_eager(T):
+    # One routing call captured in a HIP graph (one-block decode, multi-block
+    # decode with its ticket, prefill with its tile counts), replayed with
+    # eager work in between: the outputs are overwritten and another routing
+    # call runs before every replay, and each replay gives the eager result.
+    c = W.random_case(T, seed=90 + T, off=336, cnt=112)
+    other = W.random_case(100, seed=5)
+    say(f"case graph replays T={T}")
+    lg, bs = to_dev(c.logits), to_dev(c.bias)
+    e_out = M.local_num_experts(896, 16, c.off, c.cnt)
+    eager = to_numpy(M.route_local(lg, bs, c.off, c.cnt))
+    out = M.alloc_outputs(T, 16, e_out, DEV)
+    ws = torch.zeros(M.lib().moe_route_workspace_bytes(T, e_out, 16), dtype=torch.uint8,
+                     device=DEV)
+    side = torch.cuda.Stream()  # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        M.route_local(lg, bs, c.off, c.cnt, out=out, ws=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        M.route_local(lg, bs, c.off, c.cnt, out=out, ws=ws)
+    keys = ("topk_ids", "topk_weights", "packed", "counts", "offsets", "perm", "inv_perm")
+    for rep in range(4):
+        for k in keys:
+            out[k].fill_(-1)
+        run_case(other)  # eager routing between replays
+        g.replay()
+        torch.cuda.synchronize()
+        got = to_numpy(out)
+        for k in keys:
+            assert np.array_equal(got[k], eager[k]), f"replay {rep}: {k} differs"
+    assert int(ws[:256].count_nonzero()) == 0, "control block not left zeroed"
+
+
 def test_deterministic_across_calls():
     c = W.long_prefill(T=8192)
     say("case determinism T=8192")
