@@ -76,3 +76,35 @@ def test_largest_accepted_then_one_beyond_is_rejected():
     with pytest.raises(M.MoeRouteError, match="static 16 MiB"):
         M.route_local_noalloc(logits, bias)
     _check(W.random_case(64, seed=40, off=0, cnt=0))   # later calls still work
+
+
+@pytest.mark.parametrize("T", [16, 4099])
+def test_captured_in_a_graph(T):
+    # The callers this entry point is for capture it in HIP graphs: each replay
+    # (with eager routing and overwritten outputs in between) gives the
+    # workspace entry point's result.
+    c = W.random_case(T, seed=41 + T, off=336, cnt=112)
+    say(f"case noalloc graph replays T={T}")
+    logits, bias = to_dev(c.logits), to_dev(c.bias)
+    ref = to_numpy(M.route_local(logits, bias, c.off, c.cnt))
+    out = M.alloc_outputs(T, 16, int(ref["num_experts_out"]), DEV)
+    side = torch.cuda.Stream()  # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        M.route_local_noalloc(logits, bias, c.off, c.cnt, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        M.route_local_noalloc(logits, bias, c.off, c.cnt, out=out)
+    other = W.random_case(100, seed=5)
+    for rep in range(3):
+        for k in NAMES:
+            out[k].fill_(-1)
+        M.route_local(to_dev(other.logits), to_dev(other.bias))  # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        got = to_numpy(out)
+        for k in NAMES:
+            assert np.array_equal(got[k].view(np.uint32), ref[k].view(np.uint32)), \
+                f"replay {rep}: {k} differs from moe_route_local"
