@@ -52,8 +52,8 @@ def log(msg: str) -> None:
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--decode-calls", type=int, default=1000)
     ap.add_argument("--oracle-seconds", type=float, default=12.0)
     ap.add_argument("--skip-oracle", action="store_true")
