@@ -441,9 +441,25 @@ def main():
         gl_fn()
         gl_us = time_calls(gl_fn, 200)
         gl_graph_us = time_graph(gl_fn, 200)
+        # the routing with the layout written by its own scatter
+        # (moe_route_local_grouped), against the routing then the layout call
+        fused = M.route_local_grouped(lg[0], bs[0], off, cnt, tile_m=tile, rows=rows)
+        fu_fn = (lambda tile=tile, fused=fused:
+                 M.route_local_grouped(lg[0], bs[0], off, cnt, tile_m=tile, rows=rows,
+                                       out=fused, ws=ws))
+        rt_fn = lambda: M.route_local(lg[0], bs[0], off, cnt, out=out, ws=ws)
+        two_fn = (lambda tile=tile, lay=lay:
+                  (rt_fn(), M.grouped_layout(out["counts"], out["perm"], tile, out=lay)))
+        fu_fn()
         grouped[f"tile{tile}"] = {"us_per_call": round(gl_us, 2),
                                   "us_per_call_hipgraph": round(gl_graph_us, 2), "rows": rows,
-                                  "gbps_hipgraph": round(gl_bytes / (gl_graph_us * 1e-6) / 1e9, 1)}
+                                  "gbps_hipgraph": round(gl_bytes / (gl_graph_us * 1e-6) / 1e9, 1),
+                                  "route_then_layout_us_per_call_hipgraph":
+                                      round(time_graph(two_fn, 50), 2),
+                                  "route_with_fused_layout_us_per_call_hipgraph":
+                                      round(time_graph(fu_fn, 50), 2),
+                                  "route_alone_us_per_call_hipgraph":
+                                      round(time_graph(rt_fn, 50), 2)}
 
     # static balancing plan over 8 expert-owning ranks from the global counts
     # of the long-prefill input (routed once with global ids, untimed)

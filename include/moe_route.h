@@ -259,6 +259,27 @@ int moe_grouped_layout(const int32_t *counts, const int32_t *perm, int32_t num_e
                        int32_t *m_indices, int32_t *row_entry, int64_t rows, void *stream);
 
 /*
+ * moe_route_local and the grouped-GEMM layout of its entries in one call:
+ * every output of moe_route_local, and padded_offsets, m_indices and
+ * row_entry exactly as moe_grouped_layout computes them from that call's
+ * counts and perm (the layout the expert GEMM consumes, "[Kernel] Enable
+ * Kimi-K3 SiTU on the CuteDSL MoE backend and the SM107 low-latency GEMM
+ * plan", the m_indices of its grouped GEMM). Above MOE_ROUTE_MAX_FUSED_TOKENS
+ * the routing's own permutation kernel writes the layout as it places the
+ * entries, so the layout costs no launch of its own; at decode sizes the
+ * layout kernel follows the single routing launch. Arguments, workspace and
+ * checks are those of moe_route_local and moe_grouped_layout (with n_entries
+ * = T * top_k and num_experts_out = E' of the call), all made on the host
+ * before any launch.
+ */
+int moe_route_local_grouped(const float *logits, const float *bias, int32_t num_tokens,
+                            const moe_route_params *params, int32_t local_expert_offset,
+                            int32_t num_local_experts, const moe_route_outputs *out,
+                            int32_t tile_m, int32_t *padded_offsets, int32_t *m_indices,
+                            int32_t *row_entry, int64_t rows, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/*
  * Static per-rank balancing plan for an expert-parallel dispatch that holds
  * every rank at the same number of routed entries by moving the surplus of
  * overloaded expert owners ("Add MoonEP expert-parallel arm of the Kimi-K3

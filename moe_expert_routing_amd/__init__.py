@@ -15,6 +15,7 @@ Calls (same names as the C ABI):
     local_num_experts(E, K, off, cnt)              -> moe_route_local_num_experts
     route_quant_local(logits, bias, hidden, ...)   -> moe_route_quant_local
     grouped_layout(counts, perm, tile_m, ...)      -> moe_grouped_layout
+    route_local_grouped(logits, bias, off, cnt, tile_m=...) -> moe_route_local_grouped
     balance_plan(counts, n_ranks, n_entries)       -> moe_balance_plan
     grouped_layout_rows(n_entries, E', tile_m)     -> moe_grouped_layout_rows
     sigmoid_rn32(x, mode=0)                        -> moe_sigmoid_rn32 (diagnostic)
@@ -60,6 +61,10 @@ EXPORTS = {
     "moe_route_local_noalloc": (ctypes.c_int, [_c_vp, _c_vp, _c_i32, ctypes.POINTER(RouteParams),
                                                _c_i32, _c_i32, ctypes.POINTER(RouteOutputs),
                                                _c_vp]),
+    "moe_route_local_grouped": (ctypes.c_int, [_c_vp, _c_vp, _c_i32, ctypes.POINTER(RouteParams),
+                                               _c_i32, _c_i32, ctypes.POINTER(RouteOutputs),
+                                               _c_i32, _c_vp, _c_vp, _c_vp, ctypes.c_int64,
+                                               _c_vp, ctypes.c_size_t, _c_vp]),
     "moe_router_gemm_route_workspace_bytes": (ctypes.c_size_t,
                                               [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
     "moe_router_gemm_route": (ctypes.c_int, [_c_vp, _c_vp, _c_i32, _c_i32, _c_vp, _c_vp,
@@ -441,6 +446,49 @@ def grouped_layout(counts: torch.Tensor, perm: torch.Tensor, tile_m: int, *,
                                   _stream_handle(dev))
     if st:
         _check(st, "moe_grouped_layout")
+    return out
+
+
+def route_local_grouped(logits: torch.Tensor, bias: torch.Tensor, local_expert_offset: int = 0,
+                        num_local_experts: int = 0, *, tile_m: int, n_groups: int = 8,
+                        topk_group: int = 4, top_k: int = 16, group_topn: int = 2,
+                        rows: Optional[int] = None, with_entries: bool = True,
+                        out: Optional[Dict[str, torch.Tensor]] = None,
+                        ws: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """moe_route_local_grouped: route_local's outputs plus padded_offsets,
+    m_indices and (with_entries) row_entry of the grouped-GEMM layout. rows
+    defaults to the bound moe_grouped_layout_rows."""
+    _require(logits, "logits", torch.float32, 2)
+    _require(bias, "bias", torch.float32, 1)
+    T, E = logits.shape
+    if bias.shape[0] != E:
+        raise MoeRouteError("bias must have num_experts elements")
+    e_loc = local_num_experts(E, top_k, local_expert_offset, num_local_experts)
+    e_out = e_loc if e_loc > 0 else E
+    dev = logits.device
+    need = grouped_layout_rows(T * top_k, e_out, tile_m)
+    rows = need if rows is None else rows
+    if out is None:
+        out = alloc_outputs(T, top_k, e_out, dev)
+        out["padded_offsets"] = torch.empty(e_out + 1, dtype=torch.int32, device=dev)
+        out["m_indices"] = torch.empty(rows, dtype=torch.int32, device=dev)
+        if with_entries:
+            out["row_entry"] = torch.empty(rows, dtype=torch.int32, device=dev)
+    sh = _stream_handle(dev)
+    if ws is None:  # a caller's workspace is checked by the library itself
+        ws = workspace(dev, lib().moe_route_workspace_bytes(T, e_out, top_k), sh)
+    prm = _params_ref(E, n_groups, topk_group, top_k, group_topn)
+    o = _outputs_struct(out)
+    re = out.get("row_entry")
+    st = lib().moe_route_local_grouped(logits.data_ptr(), bias.data_ptr(), T, prm[1],
+                                       local_expert_offset, num_local_experts, ctypes.byref(o),
+                                       tile_m, out["padded_offsets"].data_ptr(),
+                                       out["m_indices"].data_ptr() if rows else None,
+                                       re.data_ptr() if re is not None and rows else None, rows,
+                                       ws.data_ptr(), ws.numel(), sh)
+    if st:
+        _check(st, "moe_route_local_grouped")
+    out["num_experts_out"] = e_out
     return out
 
 

@@ -594,12 +594,27 @@ __global__ __launch_bounds__(BLOCK) void block_prefix_kernel(int32_t *__restrict
 constexpr int SCATTER_PER_THREAD = 4;
 constexpr int SCATTER_TAB = 2048;  // LDS words for the chunk's route-block prefixes
 
+// Grouped-GEMM layout of the same call, written by the scatter itself
+// (moe_route_local_grouped): the rows of id e are padded[e] .. padded[e+1]-1,
+// padded = exclusive scan of round_up(counts, tile_m); m_idx[row] = e for the
+// first counts[e] of them and -1 for the rest and for rows past padded[E'];
+// row_entry[row] = the flat entry at that position of perm, -1 where m_idx
+// is. tile_m = 0: no layout.
+struct LayoutArgs {
+  int tile_m = 0;
+  int32_t *padded = nullptr;     // [E'+1]
+  int32_t *m_idx = nullptr;      // [rows]
+  int32_t *row_entry = nullptr;  // [rows], or nullptr
+  int64_t rows = 0;
+};
+
 __global__ __launch_bounds__(BLOCK) void scatter_kernel(
     const int32_t *__restrict__ packed, const int32_t *__restrict__ hist,
     const uint8_t *__restrict__ rank8, const int32_t *__restrict__ counts, int e_out, int nblk,
     int lg, int tokens_per_blk, int K, int64_t n, int32_t *__restrict__ offsets,
-    int32_t *__restrict__ perm, int32_t *__restrict__ inv) {
+    int32_t *__restrict__ perm, int32_t *__restrict__ inv, LayoutArgs la) {
   __shared__ int32_t offs[MOE_ROUTE_MAX_EXPERTS + 1];
+  __shared__ int32_t pad[MOE_ROUTE_MAX_EXPERTS + 1];  // padded offsets (layout only)
   __shared__ int32_t wave_tot[WAVES_PER_BLOCK];
   __shared__ int32_t tab[SCATTER_TAB];
   // consecutive entry chunks go to blocks on one XCD (block b runs on XCD
@@ -662,6 +677,15 @@ __global__ __launch_bounds__(BLOCK) void scatter_kernel(
   scan_store(cv, e_out, offs, wave_tot);  // its barriers also publish tab
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i <= e_out; i += BLOCK) offsets[i] = offs[i];
+  const bool layout = la.tile_m > 0;  // block-uniform
+  if (layout) {
+    int pv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) pv[k] = (cv[k] + la.tile_m - 1) / la.tile_m * la.tile_m;
+    scan_store(pv, e_out, pad, wave_tot);
+    if (blockIdx.x == 0)
+      for (int i = threadIdx.x; i <= e_out; i += BLOCK) la.padded[i] = pad[i];
+  }
 #pragma unroll
   for (int k = 0; k < SCATTER_PER_THREAD; ++k) {
     const int f = fb + (int)threadIdx.x + k * BLOCK;
@@ -670,6 +694,44 @@ __global__ __launch_bounds__(BLOCK) void scatter_kernel(
       const int32_t pos = offs[ev[k]] + h + rv[k];
       perm[pos] = f;
       if (inv) inv[f] = pos;
+      if (layout && la.row_entry) la.row_entry[pad[ev[k]] + h + rv[k]] = f;
+    }
+  }
+  if (layout) {
+    // this block's share of the layout rows, four consecutive rows per
+    // thread: the id of each (one binary search over pad for the first, then
+    // steps), and row_entry = -1 for the padding and spare rows (the entry
+    // rows' row_entry was written above)
+    const int64_t groups = (la.rows + 3) / 4;
+    const int64_t per = (groups + nb - 1) / nb;
+    const int64_t gend = min(groups, (int64_t)(b + 1) * per);
+    for (int64_t g = (int64_t)b * per + threadIdx.x; g < gend; g += BLOCK) {
+      const int64_t r0 = 4 * g;
+      int lo = 0, hi = e_out + 1;  // the largest e with pad[e] <= r0 (pad[0] = 0)
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if ((int64_t)pad[mid] <= r0) lo = mid;
+        else hi = mid;
+      }
+      int32_t mi[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int64_t r = r0 + k;
+        while (lo < e_out && (int64_t)pad[lo + 1] <= r) ++lo;
+        mi[k] = (lo < e_out && r - pad[lo] < (int64_t)(offs[lo + 1] - offs[lo])) ? lo : -1;
+      }
+      if (r0 + 4 <= la.rows && ((uintptr_t)(la.m_idx + r0) & 15) == 0) {
+        *reinterpret_cast<int4 *>(la.m_idx + r0) = make_int4(mi[0], mi[1], mi[2], mi[3]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (r0 + k < la.rows) la.m_idx[r0 + k] = mi[k];
+      }
+      if (la.row_entry) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (r0 + k < la.rows && mi[k] < 0) la.row_entry[r0 + k] = -1;
+      }
     }
   }
 }
@@ -917,7 +979,7 @@ static size_t route_ws_bytes(int T, int e_out, int K) {
 template <int NP, int LPG>
 static hipError_t launch_route(const float *logits, const float *bias, int T, const RouteParams &rp,
                                const moe_route_outputs *o, char *ws, hipStream_t st,
-                               const QuantArgs &qa) {
+                               const QuantArgs &qa, const LayoutArgs &la) {
   const int qblocks =
       qa.hidden ? (int)((qa.nchunks + QUANT_CHUNKS_PER_BLOCK - 1) / QUANT_CHUNKS_PER_BLOCK) : 0;
   if (T <= MOE_ROUTE_MAX_FUSED_TOKENS) {
@@ -961,7 +1023,7 @@ static hipError_t launch_route(const float *logits, const float *bias, int T, co
   const int64_t g3 = (n + BLOCK * SCATTER_PER_THREAD - 1) / (BLOCK * SCATTER_PER_THREAD);
   scatter_kernel<<<(int)g3, BLOCK, 0, st>>>(o->packed, pc.hist, pc.rank8, o->counts, rp.e_out,
                                             nblk, lg, tpb, rp.K, n, o->offsets, o->perm,
-                                            o->inv_perm);
+                                            o->inv_perm, la);
   return hipGetLastError();
 }
 
@@ -1021,22 +1083,22 @@ static RouteParams route_params(const moe_route_params *prm, int32_t off, int32_
 // Launches a validated call on workspace `ws`.
 static int route_launch(const float *logits, const float *bias, int32_t T, const RouteParams &rp,
                         const moe_route_outputs *o, char *ws, hipStream_t s,
-                        const QuantArgs &qa) {
+                        const QuantArgs &qa, const LayoutArgs &la = LayoutArgs{}) {
   hipError_t err;
   // the 896-expert, 8-group shape gets constant lanes per group
   if (rp.E == 896 && rp.lpg == 8) {
-    err = launch_route<7, 8>(logits, bias, T, rp, o, ws, s, qa);
+    err = launch_route<7, 8>(logits, bias, T, rp, o, ws, s, qa, la);
     return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
   }
   switch (rp.E / 128) {
-    case 1: err = launch_route<1, 0>(logits, bias, T, rp, o, ws, s, qa); break;
-    case 2: err = launch_route<2, 0>(logits, bias, T, rp, o, ws, s, qa); break;
-    case 3: err = launch_route<3, 0>(logits, bias, T, rp, o, ws, s, qa); break;
-    case 4: err = launch_route<4, 0>(logits, bias, T, rp, o, ws, s, qa); break;
-    case 5: err = launch_route<5, 0>(logits, bias, T, rp, o, ws, s, qa); break;
-    case 6: err = launch_route<6, 0>(logits, bias, T, rp, o, ws, s, qa); break;
-    case 7: err = launch_route<7, 0>(logits, bias, T, rp, o, ws, s, qa); break;
-    case 8: err = launch_route<8, 0>(logits, bias, T, rp, o, ws, s, qa); break;
+    case 1: err = launch_route<1, 0>(logits, bias, T, rp, o, ws, s, qa, la); break;
+    case 2: err = launch_route<2, 0>(logits, bias, T, rp, o, ws, s, qa, la); break;
+    case 3: err = launch_route<3, 0>(logits, bias, T, rp, o, ws, s, qa, la); break;
+    case 4: err = launch_route<4, 0>(logits, bias, T, rp, o, ws, s, qa, la); break;
+    case 5: err = launch_route<5, 0>(logits, bias, T, rp, o, ws, s, qa, la); break;
+    case 6: err = launch_route<6, 0>(logits, bias, T, rp, o, ws, s, qa, la); break;
+    case 7: err = launch_route<7, 0>(logits, bias, T, rp, o, ws, s, qa, la); break;
+    case 8: err = launch_route<8, 0>(logits, bias, T, rp, o, ws, s, qa, la); break;
     default: return MOE_ERR_UNSUPPORTED;
   }
   return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
@@ -1053,6 +1115,44 @@ static int route_impl(const float *logits, const float *bias, int32_t T,
   return route_launch(logits, bias, T, route_params(prm, off, cnt, e_out), o,
                       reinterpret_cast<char *>(workspace), reinterpret_cast<hipStream_t>(stream),
                       qa);
+}
+
+// moe_route_local_grouped: the routing call and the grouped-GEMM layout of
+// its entries. Above the decode cap the scatter writes the layout as it
+// places the entries (no layout launch); at decode sizes the layout kernel
+// follows the single routing launch.
+static int route_grouped_impl(const float *logits, const float *bias, int32_t T,
+                              const moe_route_params *prm, int32_t off, int32_t cnt,
+                              const moe_route_outputs *o, int32_t tile_m,
+                              int32_t *padded_offsets, int32_t *m_indices, int32_t *row_entry,
+                              int64_t rows, void *workspace, size_t ws_bytes, void *stream) {
+  int e_out = 0;
+  const int st = validate_route_call(logits, bias, T, prm, off, cnt, o, workspace, ws_bytes,
+                                     &e_out);
+  if (st != MOE_OK) return st;
+  const int64_t n = (int64_t)T * prm->top_k;
+  const int64_t need = moe_grouped_layout_rows(n, e_out, tile_m);
+  if (need < 0) return (int)need;
+  if (!padded_offsets) return MOE_ERR_NULL;
+  if (rows < need) return MOE_ERR_SHAPE;
+  if (rows > 0 && !m_indices) return MOE_ERR_NULL;
+  const RouteParams rp = route_params(prm, off, cnt, e_out);
+  char *ws = reinterpret_cast<char *>(workspace);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const QuantArgs no_quant{nullptr, nullptr, nullptr, 0};
+  if (T > MOE_ROUTE_MAX_FUSED_TOKENS) {
+    LayoutArgs la;
+    la.tile_m = tile_m;
+    la.padded = padded_offsets;
+    la.m_idx = m_indices;
+    la.row_entry = row_entry;
+    la.rows = rows;
+    return route_launch(logits, bias, T, rp, o, ws, s, no_quant, la);
+  }
+  const int r = route_launch(logits, bias, T, rp, o, ws, s, no_quant);
+  if (r != MOE_OK) return r;
+  return moe_grouped_layout(o->counts, o->perm, e_out, n, tile_m, padded_offsets, m_indices,
+                            row_entry, rows, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -1160,6 +1260,17 @@ int moe_route_local(const float *logits, const float *bias, int32_t num_tokens,
                     size_t workspace_bytes, void *stream) {
   return moe::route_impl(logits, bias, num_tokens, params, local_expert_offset,
                          num_local_experts, out, workspace, workspace_bytes, stream);
+}
+
+int moe_route_local_grouped(const float *logits, const float *bias, int32_t num_tokens,
+                            const moe_route_params *params, int32_t local_expert_offset,
+                            int32_t num_local_experts, const moe_route_outputs *out,
+                            int32_t tile_m, int32_t *padded_offsets, int32_t *m_indices,
+                            int32_t *row_entry, int64_t rows, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+  return moe::route_grouped_impl(logits, bias, num_tokens, params, local_expert_offset,
+                                 num_local_experts, out, tile_m, padded_offsets, m_indices,
+                                 row_entry, rows, workspace, workspace_bytes, stream);
 }
 
 int moe_route_local_noalloc(const float *logits, const float *bias, int32_t num_tokens,

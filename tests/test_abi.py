@@ -208,6 +208,27 @@ def test_grouped_layout_validation(L):
     assert call(E=0) == ERR_SHAPE
 
 
+def test_route_grouped_validation(L):
+    # the routing checks first, then the layout's; all before any launch
+    prm = _params()
+    n = 8 * 16
+    need = n + 896 * 63  # global ids: E' = 896
+
+    def call(prm=prm, T=8, tile=64, po=FAKE, mi=FAKE, re=FAKE, rows=need, ws_bytes=1 << 20,
+             logits=FAKE):
+        return L.moe_route_local_grouped(logits, FAKE, T, ctypes.byref(prm), 0, 0,
+                                         ctypes.byref(_outs()), tile, po, mi, re, rows, FAKE,
+                                         ws_bytes, None)
+    assert call(prm=_params(K=33)) == ERR_UNSUP
+    assert call(logits=None) == ERR_NULL
+    assert call(T=100, ws_bytes=256) == ERR_WS
+    assert call(tile=0) == ERR_SHAPE
+    assert call(tile=4097) == ERR_SHAPE
+    assert call(po=None) == ERR_NULL
+    assert call(mi=None) == ERR_NULL
+    assert call(rows=need - 1) == ERR_SHAPE
+
+
 def test_sigmoid_validation(L):
     assert L.moe_sigmoid_rn32(FAKE, FAKE, -1, 0, None) == ERR_SHAPE
     assert L.moe_sigmoid_rn32(None, FAKE, 5, 0, None) == ERR_NULL

@@ -81,3 +81,28 @@ def test_grouped_layout_empty_routing():
     assert lay["padded_offsets"].cpu().tolist() == [0] * 129
     assert lay["m_indices"].shape[0] == 128 * 127
     assert (lay["m_indices"] == -1).all() and (lay["row_entry"] == -1).all()
+
+
+@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("tile", [1, 3, 128, 4096])
+def test_route_with_fused_layout(name, tile):
+    # moe_route_local_grouped: the routing outputs as moe_route_local's and
+    # the layout as moe_grouped_layout's (and the oracle's), row by row;
+    # above 64 tokens the scatter writes the layout itself. Spare rows past
+    # the bound are -1 too.
+    c, want = _case_and_oracle(name)
+    say(f"case route + fused layout {name} tile={tile}")
+    T = c.logits.shape[0]
+    rows = M.grouped_layout_rows(T * c.top_k, int(want["num_experts_out"]), tile) + 5
+    out = M.route_local_grouped(to_dev(c.logits), to_dev(c.bias), c.off, c.cnt, tile_m=tile,
+                                rows=rows)
+    torch.cuda.synchronize()
+    got = {k: (v.cpu().numpy() if isinstance(v, torch.Tensor) else v) for k, v in out.items()}
+    assert_parity(got, want, name)
+    po, mi, re = O.grouped_layout(want["counts"], want["perm"], tile, rows)
+    assert np.array_equal(got["padded_offsets"], po), "padded_offsets differ"
+    bad = np.nonzero(got["m_indices"] != mi)[0]
+    assert bad.size == 0, f"m_indices differ at rows {bad[:5].tolist()}"
+    bad = np.nonzero(got["row_entry"] != re)[0]
+    assert bad.size == 0, f"row_entry differs at rows {bad[:5].tolist()}"
+
