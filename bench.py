@@ -22,6 +22,7 @@ from __future__ import annotations
 import argparse
 import ctypes
 import hashlib
+import itertools
 import json
 import os
 import platform
@@ -52,8 +53,8 @@ def log(msg: str) -> None:
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--decode-calls", type=int, default=1000)
     ap.add_argument("--oracle-seconds", type=float, default=12.0)
     ap.add_argument("--skip-oracle", action="store_true")
@@ -442,14 +443,24 @@ def main():
         gl_us = time_calls(gl_fn, 200)
         gl_graph_us = time_graph(gl_fn, 200)
         # the routing with the layout written by its own scatter
-        # (moe_route_local_grouped), against the routing then the layout call
+        # (moe_route_local_grouped), against the routing then the layout call;
+        # the calls rotate over the 3 input sets like the timed steps (one set
+        # alone would stay in the last-level cache)
         fused = M.route_local_grouped(lg[0], bs[0], off, cnt, tile_m=tile, rows=rows)
-        fu_fn = (lambda tile=tile, fused=fused:
-                 M.route_local_grouped(lg[0], bs[0], off, cnt, tile_m=tile, rows=rows,
-                                       out=fused, ws=ws))
-        rt_fn = lambda: M.route_local(lg[0], bs[0], off, cnt, out=out, ws=ws)
-        two_fn = (lambda tile=tile, lay=lay:
-                  (rt_fn(), M.grouped_layout(out["counts"], out["perm"], tile, out=lay)))
+        ctr = itertools.count()
+
+        def rt_fn():
+            i = next(ctr) % 3
+            M.route_local(lg[i], bs[i], off, cnt, out=out, ws=ws)
+
+        def two_fn(tile=tile, lay=lay):
+            rt_fn()
+            M.grouped_layout(out["counts"], out["perm"], tile, out=lay)
+
+        def fu_fn(tile=tile, fused=fused):
+            i = next(ctr) % 3
+            M.route_local_grouped(lg[i], bs[i], off, cnt, tile_m=tile, rows=rows, out=fused,
+                                  ws=ws)
         fu_fn()
         grouped[f"tile{tile}"] = {"us_per_call": round(gl_us, 2),
                                   "us_per_call_hipgraph": round(gl_graph_us, 2), "rows": rows,
