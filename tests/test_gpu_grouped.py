@@ -106,3 +106,49 @@ def test_route_with_fused_layout(name, tile):
     bad = np.nonzero(got["row_entry"] != re)[0]
     assert bad.size == 0, f"row_entry differs at rows {bad[:5].tolist()}"
 
+
+
+@pytest.mark.parametrize("case", ["t65_without_entries", "other_shape_t777", "global_t200"])
+def test_route_with_fused_layout_edges(case):
+    # 65 tokens: the first size above the one-launch routing, where the scatter
+    # writes the layout; row_entry omitted there. 256 experts, top 8: the
+    # one-token-per-wave route kernel before the same scatter. Global ids at
+    # 200 tokens (E' = 896).
+    if case == "t65_without_entries":
+        c, tile, entries = W.random_case(65, seed=61, off=336, cnt=112), 32, False
+    elif case == "other_shape_t777":
+        c = W.random_case(777, seed=62, e=256, n_groups=8, topk_group=4, top_k=8)
+        tile, entries = 64, True
+    else:
+        c, tile, entries = W.random_case(200, seed=63), 7, True
+    want = oracle_case(c)
+    say(f"case route + fused layout {case} tile={tile}")
+    T = c.logits.shape[0]
+    rows = M.grouped_layout_rows(T * c.top_k, int(want["num_experts_out"]), tile) + 3
+    out = M.route_local_grouped(to_dev(c.logits), to_dev(c.bias), c.off, c.cnt, tile_m=tile,
+                                rows=rows, with_entries=entries, n_groups=c.n_groups,
+                                topk_group=c.topk_group, top_k=c.top_k,
+                                group_topn=c.group_topn)
+    torch.cuda.synchronize()
+    got = {k: (v.cpu().numpy() if isinstance(v, torch.Tensor) else v) for k, v in out.items()}
+    assert_parity(got, want, case)
+    po, mi, re = O.grouped_layout(want["counts"], want["perm"], tile, rows)
+    assert np.array_equal(got["padded_offsets"], po), "padded_offsets differ"
+    assert np.array_equal(got["m_indices"], mi), "m_indices differ"
+    if entries:
+        assert np.array_equal(got["row_entry"], re), "row_entry differs"
+    else:
+        assert "row_entry" not in got
+
+
+def test_route_with_fused_layout_empty():
+    # no tokens: zero padded offsets, every row -1
+    logits = torch.zeros((0, 896), dtype=torch.float32, device=DEV)
+    bias = torch.zeros(896, dtype=torch.float32, device=DEV)
+    say("case route + fused layout empty")
+    out = M.route_local_grouped(logits, bias, 336, 112, tile_m=16)
+    torch.cuda.synchronize()
+    assert out["padded_offsets"].cpu().tolist() == [0] * 129
+    assert out["m_indices"].shape[0] == 128 * 15
+    assert (out["m_indices"] == -1).all() and (out["row_entry"] == -1).all()
+    assert (out["counts"] == 0).all() and (out["offsets"] == 0).all()
